@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for AB-Attention block-sparse attention (test infrastructure).
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this package.  The HIP library never calls it and shares no code
+with it.
+"""
+from .absa_oracle import *  # noqa: F401,F403
+from .absa_oracle import __all__  # noqa: F401
