@@ -1,0 +1,193 @@
+"""Throughput of the AB-Attention hot path on one MI355X.
+
+One step = block selection (KV block means, in-block k-means, block scoring, SIP capping /
+Philox draws / compaction) followed by gather-attention over the selected blocks, on the
+Wan2.1-14B-shaped 720p workload (B=1, H=40, grid 21x45x80 = 75 600 tokens, d=128, query
+block 128, KV block 16, IBCS 4 clusters x 3 k-means steps) with synthetic seeded inputs
+already resident in HBM.
+
+Prints one JSON line: value = dense-equivalent attention TFLOP/s of the whole step
+(4 B H L^2 d per step / step time).  ``roofline`` covers the dominant kernel (gather-attention):
+its algorithmic MFMA FLOPs (4 n_q d per kept key per row) over its average launch time, measured
+with HIP events on the stream it runs on.  ``cpu_baseline`` times the fp64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--keep", type=float, default=0.095)
+    ap.add_argument("--kv-block", type=int, default=16)
+    ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=640)
+    ap.add_argument("--extra", action="store_true", help="also time dense and top-k ablations")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, keep, kv_block, nrows):
+    """fp64 oracle on a bounded sample: S1 for one head plus S2-S6 for ``nrows`` seeded rows,
+    extrapolated to the whole workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    Bq, d, L = wl.q_block, wl.d, wl.L
+    NQ, NK = O.num_blocks(L, Bq), O.num_blocks(L, kv_block)
+    BH = wl.B * wl.H
+    sigma = 1.0 / math.sqrt(d)
+    keep32 = float(np.float32(keep))
+    rng = np.random.default_rng(12345)
+    rows = sorted(int(r) for r in rng.choice(BH * NQ, size=nrows, replace=False))
+    t0 = time.perf_counter()
+    O.kv_block_means(wl.k[0, rows[0] // NQ], kv_block)
+    t_s1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    res = O.select(wl.q, wl.k, Bq, kv_block, keep32, seed=0, rows=rows)
+    lists = {int(r): (res.kv_idx[i], res.inv_pi[i]) for i, r in enumerate(res.rows)}
+    O.attend_rows(wl.q, wl.k, wl.v, Bq, kv_block, lists, sigma)
+    t_rows = time.perf_counter() - t0
+    # the per-row timing above includes S1 of each sampled head once; remove it
+    heads = len(set(r // NQ for r in rows))
+    per_row = max(t_rows - heads * t_s1, 1e-9) / len(rows)
+    full_s = BH * t_s1 + BH * NQ * per_row
+    dense_flops = 4.0 * wl.B * wl.H * float(L) ** 2 * d
+    return {"value": dense_flops / full_s / 1e12, "unit": "dense-equivalent TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: KV block means of one head ({t_s1:.2f} s) and selection + "
+                       f"1/pi-weighted attention of {len(rows)} seeded rows ({t_rows:.2f} s) of the "
+                       f"same workload, extrapolated to {BH} heads x {NQ} query blocks "
+                       f"({full_s:.0f} s)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (heads shard "
+              f"across GPUs with no communication; run one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_34_amd as absa
+    from workloads import gen_config
+
+    heads = list(range(args.heads)) if args.heads else None
+    t0 = time.perf_counter()
+    wl = gen_config(3, heads=heads, kv_block=args.kv_block)
+    print(f"[bench] generated {wl.name} H={wl.H} L={wl.L} in {time.perf_counter() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    p = absa.Problem(wl.B, wl.H, wl.L, wl.d, wl.T, wl.Hs, wl.Ws, wl.q_block, args.kv_block)
+    dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)  # noqa: E731
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    lists = absa.alloc_lists(p)
+    o = torch.empty((p.B, p.H, p.L, p.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(absa.select_workspace_bytes(p, args.keep), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
+        absa.attend(p, q, k, v, lists, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
+        ev[s][1].record(stream)
+        absa.attend(p, q, k, v, lists, out=o)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    sel_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    att_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # work the attend launch did, from the lists it consumed
+    count = lists.count.long()
+    NQ, NK, L, d, Bq, Bk = p.nq, p.nk, p.L, p.d, p.q_block, p.kv_block
+    rows = torch.arange(p.rows, device="cuda")
+    nq_valid = torch.clamp(L - (rows % NQ) * Bq, max=Bq).double()
+    cap = lists.kv_idx.shape[1]
+    mask = torch.arange(cap, device="cuda")[None, :] < count[:, None]
+    blk = lists.kv_idx.long()
+    nk_valid = torch.clamp(L - blk * Bk, max=Bk).double() * mask
+    kept_keys = nk_valid.sum(dim=1)
+    alg_flops = float((4.0 * nq_valid * d * kept_keys).sum())
+    tiles = (count * Bk + 63) // 64
+    exec_flops = float((4.0 * Bq * 64 * d * tiles.double()).sum())
+    alg_bytes = float(kept_keys.sum()) * 4 * d  # K + V bf16 gathered per kept key
+    dense_flops = 4.0 * p.B * p.H * float(L) ** 2 * d
+    att_avg = sum(att_ms) / len(att_ms)
+    sel_avg = sum(sel_ms) / len(sel_ms)
+    achieved = alg_flops / (att_avg * 1e-3) / 1e12
+    line = {
+        "metric": "dense-equivalent attention TFLOP/s + executed-MFMA % of bf16 peak, 1 GPU",
+        "value": dense_flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Fourier-mode Q/K with outlier tokens, N(0,1) V)",
+        "config": {"workload": wl.name, "B": p.B, "H": p.H, "L": L, "d": d, "grid": [wl.T, wl.Hs, wl.Ws],
+                   "q_block": Bq, "kv_block": Bk, "keep": args.keep, "clusters": 4, "kmeans_steps": 3,
+                   "selection": "IBCS + SIP", "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "attend_ms": att_avg,
+        "select_ms": sel_avg,
+        "attend_dense_equiv_tflops": dense_flops / (att_avg * 1e-3) / 1e12,
+        "executed_mfma_frac": exec_flops / (att_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "kept_fraction": float(count.double().mean()) / NK,
+        "gather_GBs": alg_bytes / (att_avg * 1e-3) / 1e9,
+    }
+    if args.extra:
+        for _ in range(2):
+            absa.dense(p, q, k, v, out=o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            absa.dense(p, q, k, v, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / 3
+        line["dense_ms"] = dms
+        line["dense_mfma_frac"] = dense_flops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.keep, args.kv_block, args.cpu_sample_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

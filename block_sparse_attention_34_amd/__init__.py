@@ -1,0 +1,179 @@
+"""AB-Attention block-sparse attention on MI355X (gfx950): Python binding.
+
+Argument marshalling only: every step of selection and attention runs in the
+HIP kernels of ``libabsa.so`` (C ABI in ``include/absa.h``).  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU path: calls fail if
+the library is missing or a tensor is not on the GPU.
+"""
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import NamedTuple, Optional, Tuple
+
+from . import _lib
+from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
+
+__all__ = [
+    "Problem", "BlockLists", "select", "attend", "dense", "num_blocks", "select_workspace_bytes",
+    "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
+]
+
+_MODES = {"sip": SEL_SIP, "topk": SEL_TOPK, "all": SEL_ALL}
+
+
+def library() -> ctypes.CDLL:
+    return _lib.load()
+
+
+@dataclass(frozen=True)
+class Problem:
+    B: int
+    H: int
+    L: int
+    d: int
+    T: int
+    Hs: int
+    Ws: int
+    q_block: int
+    kv_block: int
+    scale: float = 0.0
+    out_bf16: bool = False
+
+    def c(self) -> _lib.AbsaProblem:
+        return _lib.AbsaProblem(self.B, self.H, self.L, self.d, self.T, self.Hs, self.Ws, self.q_block,
+                                self.kv_block, float(self.scale), int(bool(self.out_bf16)))
+
+    @property
+    def nq(self) -> int:
+        return -(-self.L // self.q_block)
+
+    @property
+    def nk(self) -> int:
+        return -(-self.L // self.kv_block)
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.H * self.nq
+
+    @property
+    def sigma(self) -> float:
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(self.d)
+
+
+class BlockLists(NamedTuple):
+    count: "object"   # torch.int32 [rows]
+    kv_idx: "object"  # torch.int32 [rows, cap]
+    inv_pi: "object"  # torch.float32 [rows, cap]
+
+    def c(self) -> _lib.AbsaBlockList:
+        return _lib.AbsaBlockList(self.count.data_ptr(), self.kv_idx.data_ptr(), self.inv_pi.data_ptr(),
+                                  int(self.kv_idx.shape[1]))
+
+
+def _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode):
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    return _lib.AbsaSelectParams(float(keep), int(clusters), int(kmeans_steps), float(select_scale_log2),
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, int(stream_id) & 0xFFFFFFFF, m)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_qkv(prob: Problem, *ts):
+    import torch
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("Q, K, V must be bfloat16 tensors on the GPU")
+        if not t.is_contiguous() or tuple(t.shape) != (prob.B, prob.H, prob.L, prob.d):
+            raise ValueError(f"expected contiguous [B,H,L,d] = {(prob.B, prob.H, prob.L, prob.d)}, "
+                             f"got {tuple(t.shape)}")
+
+
+def num_blocks(prob: Problem) -> Tuple[int, int]:
+    nq, nk = ctypes.c_int32(), ctypes.c_int32()
+    p = prob.c()
+    _lib.check(library().absa_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk)),
+               "absa_num_blocks")
+    return nq.value, nk.value
+
+
+def select_workspace_bytes(prob: Problem, keep: float, clusters: int = 0, kmeans_steps: int = 0,
+                           select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0,
+                           mode="sip") -> int:
+    n = ctypes.c_size_t()
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    _lib.check(library().absa_select_workspace(ctypes.byref(p), ctypes.byref(sp), ctypes.byref(n)),
+               "absa_select_workspace")
+    return n.value
+
+
+def workspace_layout(prob: Problem, keep: float, clusters: int = 0, kmeans_steps: int = 0,
+                     mode="sip") -> Tuple[int, int, int, int]:
+    offs = (ctypes.c_size_t * 4)()
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, 0.0, 0, 0, mode)
+    _lib.check(library().absa_select_workspace_layout(ctypes.byref(p), ctypes.byref(sp), offs),
+               "absa_select_workspace_layout")
+    return tuple(int(x) for x in offs)
+
+
+def alloc_lists(prob: Problem, device="cuda", cap: Optional[int] = None) -> BlockLists:
+    import torch
+    cap = prob.nk if cap is None else cap
+    return BlockLists(torch.zeros(prob.rows, dtype=torch.int32, device=device),
+                      torch.zeros((prob.rows, cap), dtype=torch.int32, device=device),
+                      torch.zeros((prob.rows, cap), dtype=torch.float32, device=device))
+
+
+def select(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmeans_steps: int = 0,
+           select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0, mode="sip",
+           lists: Optional[BlockLists] = None, want_pi: bool = False, workspace=None):
+    """IBCS + SIP (or TOPK / ALL) block selection.  Returns (lists, pi or None, workspace)."""
+    import torch
+    _check_qkv(prob, q, k)
+    lists = alloc_lists(prob, q.device) if lists is None else lists
+    pi = torch.empty((prob.rows, prob.nk), dtype=torch.float32, device=q.device) if want_pi else None
+    nbytes = select_workspace_bytes(prob, keep, clusters, kmeans_steps, select_scale_log2, seed,
+                                    stream_id, mode)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    bl = lists.c()
+    st = library().absa_select(ctypes.byref(p), ctypes.byref(sp), q.data_ptr(), k.data_ptr(),
+                               ctypes.byref(bl), pi.data_ptr() if pi is not None else None,
+                               workspace.data_ptr(), workspace.numel(), _stream())
+    _lib.check(st, "absa_select")
+    return lists, pi, workspace
+
+
+def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):
+    """Block-sparse attention over ``lists`` with 1/pi weights.  Returns O [B,H,L,d]."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    p = prob.c()
+    bl = lists.c()
+    st = library().absa_attend(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
+                               out.data_ptr(), _stream())
+    _lib.check(st, "absa_attend")
+    return out
+
+
+def dense(prob: Problem, q, k, v, out=None):
+    """Dense attention softmax(scale Q K^T) V.  Returns O [B,H,L,d]."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    p = prob.c()
+    st = library().absa_dense(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              _stream())
+    _lib.check(st, "absa_dense")
+    return out

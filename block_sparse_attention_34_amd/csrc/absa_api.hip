@@ -1,0 +1,265 @@
+// C-ABI entry points: argument validation, workspace layout, launches on the
+// caller's stream.  Declarations and the contract are in include/absa.h.
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "absa.h"
+#include "absa_launch.h"
+
+namespace {
+
+constexpr int kMaxNK = 12288;  // selection keeps one row of scores in LDS
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Dims {
+  int64_t BH, rows;
+  int NQ, NK, NKp;
+};
+
+absa_status check_problem(const absa_problem* p, Dims* dm) {
+  if (!p) return ABSA_ERR_INVALID_ARG;
+  if (p->B <= 0 || p->H <= 0 || p->L <= 0 || p->d <= 0 || p->T <= 0 || p->Hs <= 0 || p->Ws <= 0 ||
+      p->q_block <= 0 || p->kv_block <= 0)
+    return ABSA_ERR_SHAPE;
+  if ((int64_t)p->T * p->Hs * p->Ws != (int64_t)p->L) return ABSA_ERR_SHAPE;
+  if (std::isnan(p->scale) || std::isinf(p->scale)) return ABSA_ERR_INVALID_ARG;
+  if (p->out_bf16 != 0 && p->out_bf16 != 1) return ABSA_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return ABSA_ERR_UNSUPPORTED;
+  if (p->q_block != 64 && p->q_block != 128) return ABSA_ERR_UNSUPPORTED;
+  if (p->kv_block != 16 && p->kv_block != 32 && p->kv_block != 64) return ABSA_ERR_UNSUPPORTED;
+  const int64_t BH = (int64_t)p->B * p->H;
+  // element offsets are computed in 64-bit; row and key indices in 32-bit
+  if (BH * (int64_t)p->L * p->d > (int64_t(1) << 46)) return ABSA_ERR_UNSUPPORTED;
+  const int NQ = (p->L + p->q_block - 1) / p->q_block;
+  const int NK = (p->L + p->kv_block - 1) / p->kv_block;
+  if (BH * NQ > INT32_MAX / 2) return ABSA_ERR_UNSUPPORTED;
+  if (dm) {
+    dm->BH = BH;
+    dm->NQ = NQ;
+    dm->NK = NK;
+    dm->NKp = (NK + 63) / 64 * 64;
+    dm->rows = BH * NQ;
+  }
+  return ABSA_OK;
+}
+
+struct SelParams {
+  float keep, alpha;
+  int C, Tk, mode;
+};
+
+absa_status check_params(const absa_problem* p, const absa_select_params* s, SelParams* out) {
+  if (!s) return ABSA_ERR_INVALID_ARG;
+  if (!(s->keep > 0.f && s->keep <= 1.f)) return ABSA_ERR_INVALID_ARG;  // also rejects NaN
+  if (std::isnan(s->select_scale_log2) || std::isinf(s->select_scale_log2)) return ABSA_ERR_INVALID_ARG;
+  if (s->mode < ABSA_SEL_SIP || s->mode > ABSA_SEL_ALL) return ABSA_ERR_INVALID_ARG;
+  const int C = s->clusters == 0 ? 4 : s->clusters;
+  const int Tk = s->kmeans_steps == 0 ? 3 : s->kmeans_steps;
+  if (C < 0 || Tk < 0 || Tk > 64) return ABSA_ERR_INVALID_ARG;
+  if (C != 1 && C != 2 && C != 4 && C != 8) return ABSA_ERR_UNSUPPORTED;
+  if (C > p->q_block) return ABSA_ERR_UNSUPPORTED;
+  const float scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+  const float alpha = s->select_scale_log2 > 0.f ? s->select_scale_log2
+                                                 : (float)((double)scale * 1.4426950408889634);
+  if (out) *out = SelParams{s->keep, alpha, C, Tk, s->mode};
+  return ABSA_OK;
+}
+
+struct WsLayout {
+  size_t off[4];
+  size_t total;
+};
+
+WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
+  WsLayout w;
+  size_t o = 0;
+  w.off[0] = o;
+  o = align_up(o + (size_t)dm.BH * p->d * dm.NKp * sizeof(float), kWsAlign);
+  w.off[1] = o;
+  o = align_up(o + (size_t)dm.rows * C * p->d * sizeof(float), kWsAlign);
+  w.off[2] = o;
+  o = align_up(o + (size_t)dm.rows * C * sizeof(int32_t), kWsAlign);
+  w.off[3] = o;
+  o = align_up(o + (size_t)dm.rows * dm.NK * sizeof(float), kWsAlign);
+  w.total = o;
+  return w;
+}
+
+absa_status check_lists(const absa_blocklist* l, bool need_cap_nk, int NK) {
+  if (!l || !l->count || !l->kv_idx || !l->inv_pi) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(l->count, 4) || !aligned(l->kv_idx, 4) || !aligned(l->inv_pi, 4)) return ABSA_ERR_ALIGNMENT;
+  if (l->cap <= 0) return ABSA_ERR_SHAPE;
+  if (need_cap_nk && l->cap < NK) return ABSA_ERR_SHAPE;
+  return ABSA_OK;
+}
+
+std::once_flag g_attr_once;
+hipError_t g_attr_err = hipSuccess;
+
+}  // namespace
+
+extern "C" {
+
+int32_t absa_version(void) { return ABSA_VERSION; }
+
+const char* absa_status_string(int32_t status) {
+  switch (status) {
+    case ABSA_OK: return "ok";
+    case ABSA_ERR_INVALID_ARG: return "invalid argument";
+    case ABSA_ERR_SHAPE: return "inconsistent shape";
+    case ABSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ABSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case ABSA_ERR_HIP: return "HIP runtime error";
+    case ABSA_ERR_ALIGNMENT: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+absa_status absa_num_blocks(const absa_problem* prob, int32_t* nq, int32_t* nk) {
+  if (!nq || !nk) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  *nq = dm.NQ;
+  *nk = dm.NK;
+  return ABSA_OK;
+}
+
+absa_status absa_select_workspace(const absa_problem* prob, const absa_select_params* params,
+                                  size_t* bytes) {
+  if (!bytes) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  SelParams sp;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  st = check_params(prob, params, &sp);
+  if (st != ABSA_OK) return st;
+  *bytes = ws_layout(prob, dm, sp.C).total;
+  return ABSA_OK;
+}
+
+absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
+                                         size_t* offsets) {
+  if (!offsets) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  SelParams sp;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  st = check_params(prob, params, &sp);
+  if (st != ABSA_OK) return st;
+  const WsLayout w = ws_layout(prob, dm, sp.C);
+  for (int i = 0; i < 4; ++i) offsets[i] = w.off[i];
+  return ABSA_OK;
+}
+
+absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
+                        const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Dims dm;
+  SelParams sp;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  st = check_params(prob, params, &sp);
+  if (st != ABSA_OK) return st;
+  if (!q || !k) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16)) return ABSA_ERR_ALIGNMENT;
+  if (dm.NK > kMaxNK) return ABSA_ERR_UNSUPPORTED;
+  st = check_lists(out, true, dm.NK);
+  if (st != ABSA_OK) return st;
+  if (pi_out && !aligned(pi_out, 4)) return ABSA_ERR_ALIGNMENT;
+  const WsLayout w = ws_layout(prob, dm, sp.C);
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+
+  std::call_once(g_attr_once, [] { g_attr_err = absa::configure_select_kernels(); });
+  if (g_attr_err != hipSuccess) return ABSA_ERR_HIP;
+
+  char* ws = static_cast<char*>(workspace);
+  absa::SelectLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.B = prob->B;
+  a.H = prob->H;
+  a.L = prob->L;
+  a.d = prob->d;
+  a.Bq = prob->q_block;
+  a.Bk = prob->kv_block;
+  a.NQ = dm.NQ;
+  a.NK = dm.NK;
+  a.NKp = dm.NKp;
+  a.C = sp.C;
+  a.Tk = sp.Tk;
+  a.mode = sp.mode;
+  const double nstar = (double)sp.keep * (double)dm.NK;
+  a.nstar = (float)nstar;
+  const double kst = std::floor(nstar + 0.5);
+  a.kstar = (int)(kst < (double)dm.NK ? kst : (double)dm.NK);
+  a.cap = out->cap;
+  a.alpha = sp.alpha;
+  a.key0 = (uint32_t)(params->seed & 0xFFFFFFFFull);
+  a.key1 = (uint32_t)(params->seed >> 32);
+  a.ctr3 = params->stream;
+  a.kbarT = reinterpret_cast<float*>(ws + w.off[0]);
+  a.mu = reinterpret_cast<float*>(ws + w.off[1]);
+  a.nj = reinterpret_cast<int*>(ws + w.off[2]);
+  a.s = reinterpret_cast<float*>(ws + w.off[3]);
+  a.count = out->count;
+  a.kv_idx = out->kv_idx;
+  a.inv_pi = out->inv_pi;
+  a.pi_out = pi_out;
+  hipError_t e = absa::launch_select(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
+static absa_status attend_common(const absa_problem* prob, const void* q, const void* k, const void* v,
+                                 const absa_blocklist* lists, void* o, void* stream, bool dense) {
+  Dims dm;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  if (!q || !k || !v || !o) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
+  if (!dense) {
+    st = check_lists(lists, false, dm.NK);
+    if (st != ABSA_OK) return st;
+  }
+  absa::AttendLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.L = prob->L;
+  a.d = prob->d;
+  a.Bq = prob->q_block;
+  a.Bk = dense ? 64 : prob->kv_block;
+  a.NQ = dm.NQ;
+  a.NK = dense ? (prob->L + 63) / 64 : dm.NK;
+  a.rows = (int)dm.rows;
+  a.out_bf16 = prob->out_bf16;
+  const float scale = prob->scale > 0.f ? prob->scale : 1.0f / std::sqrt((float)prob->d);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (!dense) {
+    a.count = lists->count;
+    a.kv_idx = lists->kv_idx;
+    a.inv_pi = lists->inv_pi;
+    a.cap = lists->cap;
+  }
+  hipError_t e = absa::launch_attend(a, static_cast<hipStream_t>(stream), dense);
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
+absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, const void* v,
+                        const absa_blocklist* lists, void* o, void* stream) {
+  return attend_common(prob, q, k, v, lists, o, stream, false);
+}
+
+absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
+                       void* stream) {
+  return attend_common(prob, q, k, v, nullptr, o, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Launch descriptors passed from the C-ABI layer to the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace absa {
+
+struct SelectLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  int B, H, L, d, Bq, Bk, NQ, NK, NKp, C, Tk, mode, kstar, cap;
+  float nstar, alpha;
+  uint32_t key0, key1, ctr3;
+  float* kbarT;  // workspace: [BH][d][NKp]
+  float* mu;     // workspace: [rows][C][d]
+  int* nj;       // workspace: [rows][C]
+  float* s;      // workspace: [rows][NK]
+  int32_t* count;
+  int32_t* kv_idx;
+  float* inv_pi;
+  float* pi_out;  // may be null
+};
+
+struct AttendLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* count;
+  const int32_t* kv_idx;
+  const float* inv_pi;
+  void* o;
+  int L, d, Bq, Bk, NQ, NK, rows, cap, out_bf16;
+  float scale_log2;  // softmax scale times log2(e)
+};
+
+hipError_t launch_select(const SelectLaunch& a, hipStream_t st);
+hipError_t configure_select_kernels();
+hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense);
+
+}  // namespace absa

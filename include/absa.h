@@ -1,0 +1,165 @@
+/*
+ * absa.h -- C ABI of the AB-Attention block-sparse attention library (gfx950).
+ *
+ * The method (AB-Attention page, edumints blog, section "AB-Attention ve Üç
+ * Temel Yeniliği") approximates dense attention softmax(Q K^T / sqrt(d)) V
+ * (Cross-Attention glossary page, formula in its opening section) for video
+ * diffusion transformers, whose clip is one flattened spatiotemporal token
+ * sequence (VC-Attention page, opening section), in three parts:
+ *   IBCS  clusters the queries inside each query block, without permuting
+ *         tokens, and scores KV blocks from the cluster centroids;
+ *   SIP   samples KV blocks with probabilities tied to those scores and
+ *         reweights kept blocks by 1/pi in the softmax numerator and
+ *         denominator, so a single pass estimates dense attention;
+ *   a kernel that packs KV blocks much smaller than a tile into full
+ *         matrix-core tiles.
+ *
+ * The pages fix no formula for IBCS or SIP.  The rules implemented here:
+ *   KV block summary   mean of the block's valid keys;
+ *   IBCS               Lloyd k-means of the block's query vectors (squared
+ *                      Euclidean), C clusters initialised at members
+ *                      floor(j*n/C), Tk steps, ties to the lowest cluster,
+ *                      empty clusters keep their centroid;
+ *   score s_b          sum_j (n_j/n) * nk_b * 2^(l_jb - m_j) / Z_j with
+ *                      l_jb = alpha * mu_j . kbar_b, m_j = max_b l_jb, terms
+ *                      with l_jb - m_j < -64 dropped, Z_j normalising;
+ *   inclusion pi_b     min(1, lambda s_b) with sum_b pi_b = keep * NK,
+ *                      solved by iterative capping, rounded to fp32;
+ *   draw               Philox4x32-10 (Salmon et al., SC'11) with counter
+ *                      (b/4, i, b*H+h, stream) and key (seed lo, seed hi),
+ *                      word b%4, u = (x >> 8) * 2^-24, keep iff u < pi_b;
+ *   weight             w_b = fp32(1 / pi_b);
+ *   estimate           o_t = sum_{b in S} w_b sum_{k in b} e^{a_tk} v_k /
+ *                            sum_{b in S} w_b sum_{k in b} e^{a_tk},
+ *                      a_tk = scale * q_t . k_k (0 for an empty list).
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a device pointer on the current HIP device.
+ *     Struct pointers marked [host] point to host memory.
+ *   - Q, K, V are [B, H, L, d] bf16, contiguous, unpadded, 16-byte aligned.
+ *     Blocks are contiguous token ranges in the caller's order: query block i
+ *     holds tokens [i*Bq, min(L, (i+1)*Bq)), KV block b holds
+ *     [b*Bk, min(L, (b+1)*Bk)).  The last blocks may be partial; tails are
+ *     masked inside the kernels.
+ *   - A "row" is one (b, h, query block) triple; rows are ordered
+ *     (b*H + h)*NQ + i.
+ *   - The caller allocates and owns every buffer; the library allocates no
+ *     device memory and keeps no mutable global state.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL is the null
+ *     stream) and never synchronise.  Results are valid once the caller
+ *     synchronises with that stream.
+ *   - Arguments are validated before any launch; a call that fails validation
+ *     returns an error code and has no side effects.  A failed launch returns
+ *     ABSA_ERR_HIP.  No C++ exception crosses this interface.
+ */
+#ifndef ABSA_H_
+#define ABSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ABSA_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+typedef enum absa_status {
+  ABSA_OK = 0,
+  ABSA_ERR_INVALID_ARG = -1, /* null pointer, NaN or out-of-range scalar       */
+  ABSA_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. T*Hs*Ws != L)          */
+  ABSA_ERR_UNSUPPORTED = -3, /* valid but not implemented (d, block sizes, C)   */
+  ABSA_ERR_WORKSPACE = -4,   /* workspace missing or too small                  */
+  ABSA_ERR_HIP = -5,         /* a HIP runtime call or a launch failed           */
+  ABSA_ERR_ALIGNMENT = -6    /* a pointer is not aligned as required            */
+} absa_status;
+
+typedef enum absa_sel_mode {
+  ABSA_SEL_SIP = 0,  /* Poisson sampling with 1/pi weights (the method)       */
+  ABSA_SEL_TOPK = 1, /* k* = min(NK, floor(keep*NK + 1/2)) highest scores,
+                        ties to the lower block index, weight 1 (truncation
+                        baseline named in the page's "Dikkat Darboğazı"
+                        section)                                             */
+  ABSA_SEL_ALL = 2   /* every block, weight 1 (equals dense attention)        */
+} absa_sel_mode;
+
+typedef struct absa_problem {
+  int32_t B, H, L, d;        /* d in {64, 128}                                 */
+  int32_t T, Hs, Ws;         /* token grid; T*Hs*Ws must equal L               */
+  int32_t q_block;           /* Bq in {64, 128}                                */
+  int32_t kv_block;          /* Bk in {16, 32, 64}                             */
+  float scale;               /* softmax scale sigma; <= 0 selects 1/sqrt(d)    */
+  int32_t out_bf16;          /* 0: O is fp32, 1: O is bf16                      */
+} absa_problem;
+
+typedef struct absa_select_params {
+  float keep;                /* expected kept fraction of KV blocks, (0, 1]    */
+  int32_t clusters;          /* C in {1, 2, 4, 8}, C <= Bq; 0 selects 4         */
+  int32_t kmeans_steps;      /* Tk in [1, 64]; 0 selects 3                      */
+  float select_scale_log2;   /* alpha; <= 0 selects scale * log2(e)            */
+  uint64_t seed;             /* Philox key                                     */
+  uint32_t stream;           /* Philox counter word 3 (e.g. layer or step id)  */
+  int32_t mode;              /* absa_sel_mode                                  */
+} absa_select_params;
+
+/* Per-row block lists.  count[rows]; kv_idx and inv_pi are [rows][cap], row r
+ * holding count[r] entries with ascending unique block indices < NK and
+ * weights >= 1.  absa_select writes them (cap must be >= NK); absa_attend
+ * accepts any lists in this format (entries with an index >= NK are skipped,
+ * counts are clamped to [0, cap]).  All three pointers 4-byte aligned. */
+typedef struct absa_blocklist {
+  int32_t* count;
+  int32_t* kv_idx;
+  float* inv_pi;
+  int32_t cap;
+} absa_blocklist;
+
+/* Library version (ABSA_VERSION of the build). */
+int32_t absa_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* absa_status_string(int32_t status);
+
+/* NQ = ceil(L/Bq) and NK = ceil(L/Bk) for a valid problem ([host] pointers). */
+absa_status absa_num_blocks(const absa_problem* prob, int32_t* nq, int32_t* nk);
+
+/* Bytes of device workspace absa_select needs ([host] pointers). */
+absa_status absa_select_workspace(const absa_problem* prob, const absa_select_params* params,
+                                  size_t* bytes);
+
+/* Byte offsets inside the workspace of absa_select's intermediates, written
+ * by every successful absa_select call and left there for inspection:
+ *   offsets[0]  kbar^T  fp32 [B*H][d][NKp]  block mean keys, NKp = NK rounded up to 64
+ *   offsets[1]  mu      fp32 [rows][C][d]   final centroids
+ *   offsets[2]  n_j     int32 [rows][C]     final cluster sizes
+ *   offsets[3]  s       fp32 [rows][NK]     block scores
+ * ([host] pointers; offsets has 4 entries). */
+absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
+                                         size_t* offsets);
+
+/* Block selection (IBCS + SIP, or TOPK / ALL): reads Q and K, writes the
+ * lists in `out` ([host] struct, device arrays) and, when pi_out is not NULL,
+ * the fp32 inclusion probability of every block, [rows][NK] (SIP: pi_b;
+ * TOPK: 1 for kept, 0 otherwise; ALL: 1).  Requires NK <= 12288.
+ * workspace: device memory of at least absa_select_workspace() bytes, 256-byte
+ * aligned, owned by the caller, contents on entry ignored. */
+absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
+                        const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention over given lists (the estimate above): for every
+ * valid query of row r, attends to the keys of the blocks listed for r with
+ * their weights.  o is [B, H, L, d] (fp32, or bf16 if out_bf16), 16-byte
+ * aligned; only valid query rows are written.  `lists` is a [host] struct. */
+absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, const void* v,
+                        const absa_blocklist* lists, void* o, void* stream);
+
+/* Dense attention softmax(scale Q K^T) V over all L keys, same layouts. */
+absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABSA_H_ */

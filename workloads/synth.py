@@ -237,8 +237,9 @@ def gen_exact(seed: int = 0, H: int = 2, groups_collapse: bool = False) -> Workl
     <= 10), so sum_b 2^a_ij[b] is a power of two; all other channels hold -80.  Values are
     integers with |x| <= 81, exact in bf16.
 
-    ``groups_collapse``: use the same centre for all four groups (clusters then tie; exercises
-    the lowest-index tie rule and duplicate centroids).
+    ``groups_collapse``: every row of a query block equals one centre (no perturbation): all
+    distances tie, so every query joins cluster 0 (lowest-index rule) and clusters 1..3 stay
+    empty with their initial centroids.
     """
     B, d, T, Hs, Ws = 1, 64, 4, 16, 16
     L = T * Hs * Ws
@@ -286,7 +287,8 @@ def gen_exact(seed: int = 0, H: int = 2, groups_collapse: bool = False) -> Workl
                     centres.append(a)
             rows = np.zeros((Bq, d), dtype=np.float32)
             for j in range(4):
-                rows[16 * j:16 * (j + 1)] = centres[j][None, :] + zero_sum_perturb(16)
+                pert = np.zeros((16, d), np.float32) if groups_collapse else zero_sum_perturb(16)
+                rows[16 * j:16 * (j + 1)] = centres[j][None, :] + pert
             q[0, h, i * Bq:(i + 1) * Bq] = rows
     v = bf16_round(np.random.default_rng([seed, 7778]).standard_normal((B, H, L, d), dtype=np.float32))
     return Workload(q=q, k=k, v=v, B=B, H=H, L=L, d=d, T=T, Hs=Hs, Ws=Ws, q_block=Bq, kv_block=Bk,
