@@ -22,31 +22,44 @@
 
 namespace absa {
 
-// Byte offset of 16-byte chunk c of key row kk in the K tile ([64][D] bf16):
-// chunks are xor-swizzled by the row so the 16 rows read by a quarter-wave hit
-// 16 distinct bank groups.
+// LDS tiles hold 64 keys x D bf16 row-major, 16-byte chunks xor-swizzled by row.
+// K tile: chunk c of row kk at c ^ (kk & 15) (D = 128) so that the 16 rows read
+// by a quarter-wave (one 16-byte chunk each) hit distinct bank groups.
 template <int D>
 __device__ __forceinline__ int k_off(int kk, int c) {
   if constexpr (D == 128) return kk * 256 + ((c ^ (kk & 15)) << 4);
   else return kk * 128 + ((c ^ ((kk >> 1) & 7)) << 4);
 }
 
-// Byte offset of 8-byte unit u (keys 4u..4u+3) of row dc in the V^T tile
-// ([D][64] bf16, 128 bytes per row), xor-swizzled by (dc >> 1).
-__device__ __forceinline__ int vt_off(int dc, int u) { return dc * 128 + ((u ^ ((dc >> 1) & 15)) << 3); }
+// V tile: chunk c of row kk at c ^ 2(kk & 7) (D = 128).  V is read with
+// ds_read_b64_tr_b16, where a 16-lane group reads 4 consecutive rows x 32
+// bytes; the even xor keeps those 8 chunks on distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_off(int kk, int c) {
+  if constexpr (D == 128) return kk * 256 + ((c ^ ((kk & 7) << 1)) << 4);
+  else return kk * 128 + ((c ^ ((kk & 3) << 1)) << 4);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int BQ, int BK, bool DENSE, bool OUT_BF16>
-__global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
+__global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
   constexpr int NT = BQ * 2;           // BQ/32 waves of 64 lanes
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
   constexpr int NCH = 64 * CPR / NT;   // chunks per thread per tile (K and V each)
   constexpr int SPT = 64 / BK;         // list entries per 64-key tile
   constexpr int KS = D / 16;           // k-steps of the QK product
   constexpr int DB = D / 32;           // 32-wide d blocks of O
+  constexpr int TILE = 64 * D * 2;     // bytes of one K or V tile
+  // Rescale threshold (log2 units): the running max is only moved when a
+  // tile's max exceeds it by more than this, so P stays <= 2^8.
+  constexpr float TAU = 8.f;
 
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[64 * D * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char vt_lds[64 * D * 2];
-  __shared__ float bias_lds[64];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) float bias_lds[2][64];
+  __shared__ int tail_lds[2];
 
   // XCD-aware row order: workgroup w runs on XCD w % 8, so give each XCD a
   // contiguous range of rows (consecutive query blocks of the same heads share
@@ -90,9 +103,10 @@ __global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
     lw = a.inv_pi + (size_t)row * a.cap;
   }
 
-  // ---- gather of one tile into registers
+  // ---- gather of one tile into registers, and their store into an LDS buffer
   uint4 kreg[NCH], vreg[NCH];
   float bias_reg = -INFINITY;
+  bool tail_reg = false;
   auto gather = [&](int tile) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -117,31 +131,50 @@ __global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
       const int kk = tid, slot = kk / BK, r = kk % BK;
       const int e = tile * SPT + slot;
       float b = -INFINITY;
+      bool slot_ok = false;
+      int key = 0;
       if constexpr (DENSE) {
-        if (e * BK + r < a.L) b = 0.f;
+        slot_ok = true;
+        key = e * BK + r;
+        if (key < a.L) b = 0.f;
       } else if (e < nblk) {
         const int blk = lidx[e];
-        if (blk >= 0 && blk < a.NK && blk * BK + r < a.L) b = __log2f(lw[e]);
+        slot_ok = blk >= 0 && blk < a.NK;
+        key = blk * BK + r;
+        if (slot_ok && key < a.L) b = __log2f(lw[e]);
       }
       bias_reg = b;
+      tail_reg = slot_ok && key >= a.L;  // a key past L inside a listed block
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int g = tid + j * NT;
       const int kk = g / CPR, c = g % CPR;
-      *reinterpret_cast<uint4*>(k_lds + k_off<D>(kk, c)) = kreg[j];
-      const uint32_t w[4] = {vreg[j].x, vreg[j].y, vreg[j].z, vreg[j].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dc = c * 8 + e;
-        const uint16_t val = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
-        *reinterpret_cast<uint16_t*>(vt_lds + vt_off(dc, kk >> 2) + (kk & 3) * 2) = val;
-      }
+      *reinterpret_cast<uint4*>(&k_lds[buf][k_off<D>(kk, c)]) = kreg[j];
+      *reinterpret_cast<uint4*>(&v_lds[buf][v_off<D>(kk, c)]) = vreg[j];
     }
-    if (tid < 64) bias_lds[tid] = bias_reg;
+    if (wid == 0) {
+      bias_lds[buf][lane] = bias_reg;
+      const unsigned long long any_tail = __ballot(tail_reg);
+      if (lane == 0) tail_lds[buf] = any_tail != 0ull;
+    }
   };
+
+  // ---- per-lane offsets of the transposing V reads (see v_off): 16-lane group
+  // G, lane s in it; source row 4h + s/4 (+16 ks + 8 j), columns 32 db + 16 (G&1)
+  // + 4 (s&3) .. +3.
+  int voff[DB];
+  {
+    const int G = lane >> 4, s = lane & 15;
+    const int r0 = 4 * h + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (s & 3);
+      voff[db] = v_off<D>(r0, col >> 3) + (col & 7) * 2;
+    }
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -150,14 +183,21 @@ __global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
+  bf16x2 ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
 
-  if (ntiles > 0) gather(0);
+  if (ntiles > 0) {
+    gather(0);
+    stash(0);
+  }
 #pragma unroll 1
   for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();
-    stash();
-    __syncthreads();
+    const int buf = tile & 1;
+    __syncthreads();  // tile is in buf; every wave is done with buf ^ 1
     if (tile + 1 < ntiles) gather(tile + 1);
+    const unsigned char* kb = k_lds[buf];
+    const unsigned char* vb = v_lds[buf];
 
     // S^T for 64 keys (two 32-key halves) x this wave's 32 queries
     f32x16 sacc[2];
@@ -168,26 +208,55 @@ __global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
       const int kk = sb * 32 + qn;  // A-operand row (key) of this lane
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(k_lds + k_off<D>(kk, 2 * ks + h));
+        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + k_off<D>(kk, 2 * ks + h));
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], sacc[sb], 0, 0, 0);
       }
     }
-    // lane (h, qn) register r of half sb holds key 32 sb + 8 (r/4) + 4 h + r%4
+    // Lane (h, qn) register r of half sb holds key 32 sb + 8 (r/4) + 4 h + r%4.
+    // t = S scale log2(e) + log2(w_block) - m, with m the running reference.
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float mt = -INFINITY;
+    if (!tail_lds[buf]) {
+      // every 4-key group lies in one block and is all valid or all masked
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float tv = fmaf(sacc[sb][r], sl2, bias_lds[kk]);
-        sacc[sb][r] = tv;
-        mt = fmaxf(mt, tv);
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float cg = bias_lds[buf][32 * sb + 8 * g4 + 4 * h] - m_use;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float tv = fmaf(sacc[sb][4 * g4 + i], sl2, cg);
+            sacc[sb][4 * g4 + i] = tv;
+            mt = fmaxf(mt, tv);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float tv = fmaf(sacc[sb][r], sl2, bias_lds[buf][kk] - m_use);
+          sacc[sb][r] = tv;
+          mt = fmaxf(mt, tv);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // Move the reference only when needed (first valid tile, or growth > TAU).
+    if (mt > TAU || (m_run == -INFINITY && mt > -INFINITY)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-mt);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_run = m_use + mt;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] -= mt;
+    }
+    // P = 2^t rounded to bf16; the row sum adds exactly these rounded values
     bf16x8 pf[4];
     float psum = 0.f;
 #pragma unroll
@@ -195,32 +264,34 @@ __global__ __launch_bounds__(BQ * 2) void attend_kernel(AttendLaunch a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[sb][half * 8 + e] - m_use);
-          const __bf16 pb = (__bf16)p;
-          pf[sb * 2 + half][e] = pb;
-          psum += (float)pb;
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pk;
+          pk[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][half * 8 + e]);
+          pk[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][half * 8 + e + 1]);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, psum, false);
+          pf[sb * 2 + half][e] = pk[0];
+          pf[sb * 2 + half][e + 1] = pk[1];
         }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T: k-step ks covers keys 16 ks .. 16 ks + 15; this lane's 8
-    // keys are 16 ks + {4h..4h+3} and 16 ks + 8 + {4h..4h+3}, matching pf[ks].
+    // keys are 16 ks + {4h..4h+3} and 16 ks + 8 + {4h..4h+3}, matching pf[ks];
+    // the two transposing reads deliver exactly those keys for column 32 db + qn.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int dc = db * 32 + qn;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vt_lds + vt_off(dc, 4 * ks + h));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vt_lds + vt_off(dc, 4 * ks + 2 + h));
-        const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const unsigned char* p0 = vb + voff[db] + (16 * ks) * (D * 2);
+        const unsigned char* p1 = p0 + 8 * (D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+        const i16x4 w[2] = {lo, hi};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks],
                                                           acc[db], 0, 0, 0);
       }
     }
+    if (tile + 1 < ntiles) stash(buf ^ 1);
   }
 
   // ---- epilogue: O = O^T / l, valid queries only
