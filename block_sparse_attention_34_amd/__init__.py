@@ -111,8 +111,9 @@ def select_workspace_bytes(prob: Problem, keep: float, clusters: int = 0, kmeans
 
 
 def workspace_layout(prob: Problem, keep: float, clusters: int = 0, kmeans_steps: int = 0,
-                     mode="sip") -> Tuple[int, int, int, int]:
-    offs = (ctypes.c_size_t * 4)()
+                     mode="sip") -> Tuple[int, int, int, int, int]:
+    """Offsets of (kbar^T, mu, n_j, s, logits) inside the selection workspace."""
+    offs = (ctypes.c_size_t * 5)()
     p = prob.c()
     sp = _params(keep, clusters, kmeans_steps, 0.0, 0, 0, mode)
     _lib.check(library().absa_select_workspace_layout(ctypes.byref(p), ctypes.byref(sp), offs),

@@ -70,8 +70,10 @@ absa_status check_params(const absa_problem* p, const absa_select_params* s, Sel
   return ABSA_OK;
 }
 
+constexpr int kWsRegions = 5;
+
 struct WsLayout {
-  size_t off[4];
+  size_t off[kWsRegions];
   size_t total;
 };
 
@@ -86,6 +88,8 @@ WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
   o = align_up(o + (size_t)dm.rows * C * sizeof(int32_t), kWsAlign);
   w.off[3] = o;
   o = align_up(o + (size_t)dm.rows * dm.NK * sizeof(float), kWsAlign);
+  w.off[4] = o;
+  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
   w.total = o;
   return w;
 }
@@ -153,7 +157,7 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
   st = check_params(prob, params, &sp);
   if (st != ABSA_OK) return st;
   const WsLayout w = ws_layout(prob, dm, sp.C);
-  for (int i = 0; i < 4; ++i) offsets[i] = w.off[i];
+  for (int i = 0; i < kWsRegions; ++i) offsets[i] = w.off[i];
   return ABSA_OK;
 }
 
@@ -208,6 +212,7 @@ absa_status absa_select(const absa_problem* prob, const absa_select_params* para
   a.mu = reinterpret_cast<float*>(ws + w.off[1]);
   a.nj = reinterpret_cast<int*>(ws + w.off[2]);
   a.s = reinterpret_cast<float*>(ws + w.off[3]);
+  a.logit = reinterpret_cast<float*>(ws + w.off[4]);
   a.count = out->count;
   a.kv_idx = out->kv_idx;
   a.inv_pi = out->inv_pi;

@@ -16,6 +16,7 @@ struct SelectLaunch {
   float* mu;     // workspace: [rows][C][d]
   int* nj;       // workspace: [rows][C]
   float* s;      // workspace: [rows][NK]
+  float* logit;  // workspace: [rows][C][NK]
   int32_t* count;
   int32_t* kv_idx;
   float* inv_pi;

@@ -47,13 +47,22 @@ __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __re
       const int n = min(Bk, L - b * Bk);
       const uint4* src = reinterpret_cast<const uint4*>(kh + (size_t)b * Bk * D + c * 8);
 #pragma unroll 1
-      for (int r = 0; r < n; ++r) {
-        const uint4 w = src[(size_t)r * (D / 8)];
-        float lo, hi;
-        unpack_bf16x2(w.x, lo, hi); acc[0] += lo; acc[1] += hi;
-        unpack_bf16x2(w.y, lo, hi); acc[2] += lo; acc[3] += hi;
-        unpack_bf16x2(w.z, lo, hi); acc[4] += lo; acc[5] += hi;
-        unpack_bf16x2(w.w, lo, hi); acc[6] += lo; acc[7] += hi;
+      for (int r0 = 0; r0 < n; r0 += 16) {
+        uint4 wv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)  // all loads in flight before the (ordered) sums
+          wv[r] = (r0 + r < n) ? src[(size_t)(r0 + r) * (D / 8)] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (r0 + r < n) {
+            const uint4 w = wv[r];
+            float lo, hi;
+            unpack_bf16x2(w.x, lo, hi); acc[0] += lo; acc[1] += hi;
+            unpack_bf16x2(w.y, lo, hi); acc[2] += lo; acc[3] += hi;
+            unpack_bf16x2(w.z, lo, hi); acc[4] += lo; acc[5] += hi;
+            unpack_bf16x2(w.w, lo, hi); acc[6] += lo; acc[7] += hi;
+          }
+        }
       }
       const float fn = (float)n;
 #pragma unroll
@@ -94,10 +103,27 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_kernel(const uint16_t* __rest
   const int bh = row / NQ, i = row % NQ;
   const int q0 = i * Bq;
   const int n = min(Bq, L - q0);
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)bh * L + q0) * D);
-  for (int idx = t; idx < n * (D / 2); idx += 256) {
-    const int qq = idx / (D / 2), cp = idx % (D / 2);
-    X[qq * XS + cp] = src[idx];
+  {
+    // 128 x D bf16 = 128 x D/8 16-byte chunks; every load is issued before any store
+    constexpr int CH = D / 8, PER = 128 * CH / 256;
+    const uint4* src = reinterpret_cast<const uint4*>(q + ((size_t)bh * L + q0) * D);
+    uint4 wv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = t + 256 * j;
+      wv[j] = (idx / CH < n) ? src[idx] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int idx = t + 256 * j;
+      const int qq = idx / CH, cp = (idx % CH) * 4;
+      if (qq < n) {
+        X[qq * XS + cp + 0] = wv[j].x;
+        X[qq * XS + cp + 1] = wv[j].y;
+        X[qq * XS + cp + 2] = wv[j].z;
+        X[qq * XS + cp + 3] = wv[j].w;
+      }
+    }
   }
   __syncthreads();
   for (int idx = t; idx < C * D; idx += 256) {
@@ -187,151 +213,76 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_kernel(const uint16_t* __rest
 }
 
 // ============================================================================= K2b
-// Scores of every KV block for RPW = 128/C rows of one head (a 128-centroid x
-// 64-block tile per step).  Pass 1 finds each centroid's max logit and its
-// normaliser Z_j online; pass 2 recomputes the logits and writes
-// s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j (0 below the -64 floor).
-// Thread micro-tile: 8 centroids (8/C rows) x 4 blocks.
-template <int D, int C>
-__global__ __launch_bounds__(256) void ibcs_score_kernel(const float* __restrict__ kbarT,
+// Block logits l[row][j][b] = alpha * (mu_j . kbar_b) for every centroid of a
+// head against every KV block: a [NQ*C x d] x [d x NK] product on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32, fp32 products and sums).  Workgroup = 4 waves x 32
+// centroids; a wave keeps its centroids as A operands in registers and streams
+// 32-block tiles of kbar^T through LDS.  Grid (ceil(M/128), BH, nsplit): split
+// z covers a contiguous range of 32-block tiles.
+template <int D>
+__global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict__ kbarT,
                                                          const float* __restrict__ mu,
-                                                         const int* __restrict__ nj,
-                                                         float* __restrict__ s_out, int L, int Bk,
-                                                         int Bq, int NQ, int NK, int NKp,
-                                                         float alpha) {
-  constexpr int RPW = 128 / C;
-  constexpr int RPT = 8 / C;  // rows per thread
-  extern __shared__ float smem[];
-  float* muT = smem;               // [D][128]
-  float* kT = smem + D * 128;      // [D][64]
-  const int t = threadIdx.x;
-  const int tb = t & 15, tc = t >> 4;
+                                                         float* __restrict__ logit, int M, int NK,
+                                                         int NKp, int tiles_per_split, float alpha) {
+  constexpr int KS = D / 2;  // k-steps of 2 dims
+  __shared__ __attribute__((aligned(16))) float kt[2][D * 32];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
-  const int r0 = blockIdx.x * RPW;
+  const int m0 = blockIdx.x * 128 + w * 32;
+  const int tile0 = blockIdx.z * tiles_per_split;
+  const int ntile_all = NKp / 32;
+  const int tile1 = min(ntile_all, tile0 + tiles_per_split);
+  if (tile0 >= tile1) return;
 
-  for (int idx = t; idx < D * 128; idx += 256) {
-    const int cv = idx & 127, c = idx >> 7;
-    const int r = r0 + cv / C;
-    muT[c * 128 + cv] = (r < NQ) ? mu[((size_t)(bh * NQ + r) * C + (cv % C)) * D + c] : 0.f;
+  // A operands: lane (h, n) holds mu[m0 + n][2 s + h]
+  float areg[KS];
+  {
+    const int m = m0 + n;
+    const float* src = mu + ((size_t)bh * M + (m < M ? m : 0)) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) areg[s2] = (m < M) ? src[2 * s2 + h] : 0.f;
   }
   const float* kb = kbarT + (size_t)bh * D * NKp;
-  const int ntiles = NKp / 64;
-
-  float m_run[8], z_run[8];
+  float4 stage[D / 32];
+  auto fetch = [&](int tile) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a) { m_run[a] = -INFINITY; z_run[a] = 0.f; }
-
-  auto load_tile = [&](int tile) {
-    __syncthreads();
-    for (int idx = t; idx < D * 16; idx += 256) {
-      const int c = idx >> 4, b4 = idx & 15;
-      *reinterpret_cast<float4*>(kT + c * 64 + b4 * 4) =
-          *reinterpret_cast<const float4*>(kb + (size_t)c * NKp + tile * 64 + b4 * 4);
-    }
-    __syncthreads();
-  };
-  auto compute = [&](float (&acc)[8][4]) {
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < D; ++c) {
-      const float4 m0 = *reinterpret_cast<const float4*>(muT + c * 128 + tc * 8);
-      const float4 m1 = *reinterpret_cast<const float4*>(muT + c * 128 + tc * 8 + 4);
-      const float4 kv = *reinterpret_cast<const float4*>(kT + c * 64 + tb * 4);
-      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(mv[a], kk[b], acc[a][b]);
+    for (int i = 0; i < D / 32; ++i) {
+      const int idx = t + 256 * i;  // float4 index in the [D][32] tile
+      const int c = idx >> 3, b4 = idx & 7;
+      stage[i] = *reinterpret_cast<const float4*>(kb + (size_t)c * NKp + tile * 32 + b4 * 4);
     }
   };
-
-  // ---- pass 1: per-centroid max and normaliser
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int idx = t + 256 * i;
+      *reinterpret_cast<float4*>(&kt[buf][idx * 4]) = stage[i];
+    }
+  };
+  fetch(tile0);
+  put(0);
+  float* out_base = logit + (size_t)bh * M * NK;
 #pragma unroll 1
-  for (int tile = 0; tile < ntiles; ++tile) {
-    load_tile(tile);
-    float acc[8][4];
-    compute(acc);
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int buf = (tile - tile0) & 1;
+    __syncthreads();
+    if (tile + 1 < tile1) fetch(tile + 1);
+    f32x16 acc;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int blk = tile * 64 + tb * 4 + b;
-      if (blk < NK) {
-        const float nk = (float)min(Bk, L - blk * Bk);
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const float l = alpha * acc[a][b];
-          if (l > m_run[a]) {
-            z_run[a] = (m_run[a] - l >= -64.f) ? fmaf(z_run[a], exp2_split(m_run[a] - l), nk) : nk;
-            m_run[a] = l;
-          } else if (l - m_run[a] >= -64.f) {
-            z_run[a] = fmaf(nk, exp2_split(l - m_run[a]), z_run[a]);
-          }
-        }
+    for (int s2 = 0; s2 < KS; ++s2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(areg[s2], kt[buf][(2 * s2 + h) * 32 + n], acc, 0, 0, 0);
+    const int b = tile * 32 + n;
+    if (b < NK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M) out_base[(size_t)m * NK + b] = alpha * acc[r];
       }
     }
-  }
-  // combine the 16 block-groups that share these centroids (lanes 16k..16k+15)
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float m2 = __shfl_xor(m_run[a], o, 64);
-      const float z2 = __shfl_xor(z_run[a], o, 64);
-      const float m = fmaxf(m_run[a], m2);
-      float z = 0.f;
-      if (m_run[a] - m >= -64.f) z += z_run[a] * exp2_split(m_run[a] - m);
-      if (m2 - m >= -64.f) z += z2 * exp2_split(m2 - m);
-      m_run[a] = m;
-      z_run[a] = z;
-    }
-  }
-  // coefficient (n_j / n) / Z_j of each of this thread's centroids
-  float coef[8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int cv = tc * 8 + a;
-    const int r = r0 + cv / C;
-    coef[a] = 0.f;
-    if (r < NQ) {
-      const int n = min(Bq, L - r * Bq);
-      const int cnt = nj[(size_t)(bh * NQ + r) * C + (cv % C)];
-      if (cnt > 0) coef[a] = __fdiv_rn(__fdiv_rn((float)cnt, (float)n), z_run[a]);
-    }
-  }
-  // ---- pass 2: scores
-#pragma unroll 1
-  for (int tile = 0; tile < ntiles; ++tile) {
-    load_tile(tile);
-    float acc[8][4];
-    compute(acc);
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const int r = r0 + (tc * 8) / C + rr;
-      float sv[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int blk = tile * 64 + tb * 4 + b;
-        const float nk = (blk < NK) ? (float)min(Bk, L - blk * Bk) : 0.f;
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const int a = rr * C + j;
-          const float dl = alpha * acc[a][b] - m_run[a];
-          if (dl >= -64.f && coef[a] != 0.f) s = fmaf(coef[a], nk * exp2_split(dl), s);
-        }
-        sv[b] = s;
-      }
-      if (r < NQ) {
-        float* dst = s_out + (size_t)(bh * NQ + r) * NK + tile * 64 + tb * 4;
-        const int blk0 = tile * 64 + tb * 4;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (blk0 + b < NK) dst[b] = sv[b];
-      }
-    }
+    if (tile + 1 < tile1) put(buf ^ 1);
   }
 }
 
@@ -340,7 +291,11 @@ __global__ __launch_bounds__(256) void ibcs_score_kernel(const float* __restrict
 // Bernoulli draws (or top-k / all), and compaction into the row's list.
 constexpr int SIP_NT = 256;
 
-__global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ s_all, int NK, int NQ,
+template <int C>
+__global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ logit,
+                                                     const int* __restrict__ nj,
+                                                     float* __restrict__ s_out, int L, int Bq, int Bk,
+                                                     int NK, int NQ,
                                                      float nstar, int kstar, int mode, uint32_t key0,
                                                      uint32_t key1, uint32_t ctr3,
                                                      int32_t* __restrict__ count_out,
@@ -351,11 +306,105 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ s
   unsigned char* flag = reinterpret_cast<unsigned char*>(s + NK);  // [NK]
   __shared__ float redf[SIP_NT / 64];
   __shared__ int redi[SIP_NT / 64];
-  const int t = threadIdx.x;
+  __shared__ float redm[C][SIP_NT / 64], redz[C][SIP_NT / 64];
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   const int row = blockIdx.x;
   const int bh = row / NQ, i = row % NQ;
-  const float* srow = s_all + (size_t)row * NK;
-  for (int b = t; b < NK; b += SIP_NT) s[b] = srow[b];
+
+  // ---- IBCS scores of this row from its logits: per centroid the max m_j and
+  // the normaliser Z_j = sum_b nk_b 2^(l_jb - m_j) (terms below 2^-64 of the
+  // max dropped), then s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j.
+  {
+    const float* lrow = logit + (size_t)row * C * NK;
+    float mj[C], zj[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) { mj[j] = -INFINITY; zj[j] = 0.f; }
+    constexpr int U = 4;  // blocks per batch: U*C loads in flight
+#pragma unroll 1
+    for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
+      float lv[U][C];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const int b = b0 + u * SIP_NT;
+          lv[u][j] = (b < NK) ? lrow[(size_t)j * NK + b] : -INFINITY;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u * SIP_NT;
+        if (b >= NK) break;
+        const float nk = (float)min(Bk, L - b * Bk);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const float l = lv[u][j];
+          if (l > mj[j]) {
+            zj[j] = (mj[j] - l >= -64.f) ? fmaf(zj[j], exp2_split(mj[j] - l), nk) : nk;
+            mj[j] = l;
+          } else if (l - mj[j] >= -64.f) {
+            zj[j] = fmaf(nk, exp2_split(l - mj[j]), zj[j]);
+          }
+        }
+      }
+    }
+    // combine (m, Z) pairs: lanes, then waves
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(mj[j], o, 64), z2 = __shfl_xor(zj[j], o, 64);
+        const float m = fmaxf(mj[j], m2);
+        float z = 0.f;
+        if (mj[j] - m >= -64.f) z += zj[j] * exp2_split(mj[j] - m);
+        if (m2 - m >= -64.f) z += z2 * exp2_split(m2 - m);
+        mj[j] = m;
+        zj[j] = z;
+      }
+      if (lane == 0) { redm[j][wid] = mj[j]; redz[j][wid] = zj[j]; }
+    }
+    __syncthreads();
+    const int n = min(Bq, L - i * Bq);
+    float coef[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < SIP_NT / 64; ++w) m = fmaxf(m, redm[j][w]);
+      float z = 0.f;
+#pragma unroll
+      for (int w = 0; w < SIP_NT / 64; ++w)
+        if (redm[j][w] - m >= -64.f) z += redz[j][w] * exp2_split(redm[j][w] - m);
+      mj[j] = m;
+      const int cnt = nj[(size_t)row * C + j];
+      coef[j] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), z) : 0.f;
+    }
+    float* srow_out = s_out + (size_t)row * NK;
+#pragma unroll 1
+    for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
+      float lv[U][C];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const int b = b0 + u * SIP_NT;
+          lv[u][j] = (b < NK) ? lrow[(size_t)j * NK + b] : -INFINITY;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u * SIP_NT;
+        if (b >= NK) break;
+        const float nk = (float)min(Bk, L - b * Bk);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const float dl = lv[u][j] - mj[j];
+          if (dl >= -64.f && coef[j] != 0.f) acc = fmaf(coef[j], nk * exp2_split(dl), acc);
+        }
+        s[b] = acc;
+        srow_out[b] = acc;
+      }
+    }
+  }
   // contiguous chunk of P blocks per thread, P a multiple of 4
   const int P = ((NK + SIP_NT * 4 - 1) / (SIP_NT * 4)) * 4;
   const int b0 = min(NK, t * P), b1 = min(NK, b0 + P);
@@ -487,36 +536,35 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   }
   // K2b
   {
-    const int rpw = 128 / a.C;
-    dim3 grid((a.NQ + rpw - 1) / rpw, BH);
-    const size_t lds = (size_t)a.d * (128 + 64) * sizeof(float);
-#define ABSA_SCORE(DD, CC)                                                                         \
-  ibcs_score_kernel<DD, CC><<<grid, 256, lds, st>>>(a.kbarT, a.mu, a.nj, a.s, a.L, a.Bk, a.Bq, a.NQ, \
-                                                    a.NK, a.NKp, a.alpha)
-    if (a.d == 128) {
-      switch (a.C) {
-        case 1: ABSA_SCORE(128, 1); break;
-        case 2: ABSA_SCORE(128, 2); break;
-        case 4: ABSA_SCORE(128, 4); break;
-        default: ABSA_SCORE(128, 8); break;
-      }
-    } else {
-      switch (a.C) {
-        case 1: ABSA_SCORE(64, 1); break;
-        case 2: ABSA_SCORE(64, 2); break;
-        case 4: ABSA_SCORE(64, 4); break;
-        default: ABSA_SCORE(64, 8); break;
-      }
-    }
-#undef ABSA_SCORE
+    const int M = a.NQ * a.C;
+    const int mtiles = (M + 127) / 128;
+    const int ntile_all = a.NKp / 32;
+    int nsplit = (2048 + mtiles * BH - 1) / (mtiles * BH);
+    nsplit = nsplit < 1 ? 1 : (nsplit > ntile_all ? ntile_all : nsplit);
+    const int per = (ntile_all + nsplit - 1) / nsplit;
+    nsplit = (ntile_all + per - 1) / per;
+    dim3 grid(mtiles, BH, nsplit);
+    if (a.d == 128)
+      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, M, a.NK, a.NKp, per, a.alpha);
+    else
+      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, M, a.NK, a.NKp, per, a.alpha);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // K3
   {
     const size_t lds = (size_t)a.NK * (sizeof(float) + 1);
-    sip_kernel<<<rows, SIP_NT, lds, st>>>(a.s, a.NK, a.NQ, a.nstar, a.kstar, a.mode, a.key0, a.key1,
-                                          a.ctr3, a.count, a.kv_idx, a.inv_pi, a.cap, a.pi_out);
+#define ABSA_SIP(CC)                                                                                  \
+  sip_kernel<CC><<<rows, SIP_NT, lds, st>>>(a.logit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK, a.NQ, a.nstar,  \
+                                            a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
+                                            a.inv_pi, a.cap, a.pi_out)
+    switch (a.C) {
+      case 1: ABSA_SIP(1); break;
+      case 2: ABSA_SIP(2); break;
+      case 4: ABSA_SIP(4); break;
+      default: ABSA_SIP(8); break;
+    }
+#undef ABSA_SIP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -524,19 +572,15 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
 }
 
 hipError_t configure_select_kernels() {
-  // The scoring kernel uses 96 KB of dynamic LDS at d = 128.
-  const int lds128 = 128 * (128 + 64) * (int)sizeof(float);
+  // The SIP kernel keeps one row of scores and flags in LDS: up to 60 KB.
   hipError_t e;
-#define ABSA_ATTR(DD, CC)                                                                  \
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ibcs_score_kernel<DD, CC>),      \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds128);             \
+#define ABSA_ATTR(CC)                                                                   \
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sip_kernel<CC>),              \
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 12288 * 5);      \
   if (e != hipSuccess) return e;
-  ABSA_ATTR(128, 1) ABSA_ATTR(128, 2) ABSA_ATTR(128, 4) ABSA_ATTR(128, 8)
-  ABSA_ATTR(64, 1) ABSA_ATTR(64, 2) ABSA_ATTR(64, 4) ABSA_ATTR(64, 8)
+  ABSA_ATTR(1) ABSA_ATTR(2) ABSA_ATTR(4) ABSA_ATTR(8)
 #undef ABSA_ATTR
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sip_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 12288 * 5);
-  return e;
+  return hipSuccess;
 }
 
 }  // namespace absa

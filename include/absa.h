@@ -133,7 +133,8 @@ absa_status absa_select_workspace(const absa_problem* prob, const absa_select_pa
  *   offsets[1]  mu      fp32 [rows][C][d]   final centroids
  *   offsets[2]  n_j     int32 [rows][C]     final cluster sizes
  *   offsets[3]  s       fp32 [rows][NK]     block scores
- * ([host] pointers; offsets has 4 entries). */
+ *   offsets[4]  l       fp32 [rows][C][NK]  block logits alpha * mu_j . kbar_b
+ * ([host] pointers; offsets has 5 entries). */
 absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
                                          size_t* offsets);
 

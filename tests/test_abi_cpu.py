@@ -108,11 +108,12 @@ def test_num_blocks_and_shape_errors(lib):
 def test_workspace_size_and_layout(lib):
     n = ctypes.c_size_t()
     assert lib.absa_select_workspace(ctypes.byref(prob()), ctypes.byref(params()), ctypes.byref(n)) == 0
-    offs = (ctypes.c_size_t * 4)()
+    offs = (ctypes.c_size_t * 5)()
     assert lib.absa_select_workspace_layout(ctypes.byref(prob()), ctypes.byref(params()), offs) == 0
-    # kbar^T [2][64][64] f32, mu [32][4][64] f32, n_j [32][4] i32, s [32][64] f32, 256-aligned
-    assert list(offs) == [0, 32768, 32768 + 32768, 65536 + 512]
-    assert n.value == 65536 + 512 + 32 * 64 * 4
+    # kbar^T [2][64][64] f32, mu [32][4][64] f32, n_j [32][4] i32, s [32][64] f32,
+    # logits [32][4][64] f32, each 256-aligned
+    assert list(offs) == [0, 32768, 32768 + 32768, 65536 + 512, 65536 + 512 + 8192]
+    assert n.value == 65536 + 512 + 8192 + 32 * 4 * 64 * 4
     for bad, code in ((dict(keep=0.0), -1), (dict(keep=1.5), -1), (dict(keep=float("nan")), -1),
                       (dict(clusters=3), -3), (dict(clusters=-1), -1), (dict(kmeans_steps=65), -1),
                       (dict(mode=7), -1), (dict(select_scale_log2=float("inf")), -1)):
