@@ -42,9 +42,10 @@ __device__ __forceinline__ int v_off(int kk, int c) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a first-class vector, kept in VGPRs
 
 template <int D, int BQ, int BK, bool DENSE, bool OUT_BF16>
-__global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
+__global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLaunch a) {
   constexpr int NT = BQ * 2;           // BQ/32 waves of 64 lanes
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
   constexpr int NCH = 64 * CPR / NT;   // chunks per thread per tile (K and V each)
@@ -61,11 +62,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
   __shared__ __attribute__((aligned(16))) float bias_lds[2][64];
   __shared__ int tail_lds[2];
 
-  // XCD-aware row order: workgroup w runs on XCD w % 8, so give each XCD a
-  // contiguous range of rows (consecutive query blocks of the same heads share
-  // their KV blocks through that XCD's L2).
-  const int nper = (a.rows + 7) >> 3;
-  const int row = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+  // Rows in order: consecutive workgroups (dispatched round-robin over the 8
+  // XCDs) take consecutive query blocks of one head, so all XCDs work on the
+  // same head's K/V at a time and it stays resident in the shared last-level
+  // cache (one head of the 720p workload is 39 MB; eight heads would not fit).
+  const int row = blockIdx.x;
   if (row >= a.rows) return;
   const int bh = row / a.NQ, qb = row % a.NQ;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -103,47 +104,63 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
     lw = a.inv_pi + (size_t)row * a.cap;
   }
 
-  // ---- gather of one tile into registers, and their store into an LDS buffer
-  uint4 kreg[NCH], vreg[NCH];
+  // ---- gather of one tile into registers, and their store into an LDS buffer.
+  // The list entries a tile needs are fetched one iteration before its K/V
+  // loads are issued, so no K/V load waits on a list load.  K/V loads are
+  // unconditional: a masked key reads row 0 of the head (in bounds, finite) and
+  // its -inf bias removes it from the softmax.
+  // Raw list entries: *_cur for the tile whose K/V loads are issued next,
+  // *_nxt for the one after.  The loads of *_nxt are issued before the K/V loads
+  // and only read an iteration later (memory waits retire in issue order, so a
+  // list load issued after the K/V loads would hold them up).
+  int nb_cur[NCH], nb_nxt[NCH];
+  int nbb_cur = 0, nbb_nxt = 0;        // threads 0..63: block of key `tid`
+  float nbw_cur = 1.f, nbw_nxt = 1.f;  // and its weight
+  auto fetch_idx = [&](int tile) {     // raw entries of `tile` into *_nxt
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int e = tile * SPT + ((tid + j * NT) / CPR) / BK;
+        const int ec = e < nblk ? e : nblk - 1;
+        nb_nxt[j] = lidx[ec < 0 ? 0 : ec];
+      }
+      if (tid < 64) {
+        const int e = tile * SPT + tid / BK;
+        const int ec = e < nblk ? e : nblk - 1;
+        nbb_nxt = lidx[ec < 0 ? 0 : ec];
+        nbw_nxt = lw[ec < 0 ? 0 : ec];
+      }
+    }
+  };
+  auto rotate_idx = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) nb_cur[j] = nb_nxt[j];
+    nbb_cur = nbb_nxt;
+    nbw_cur = nbw_nxt;
+  };
+  u32x4 kreg[NCH], vreg[NCH];
   float bias_reg = -INFINITY;
   bool tail_reg = false;
-  auto gather = [&](int tile) {
+  auto gather = [&](int tile) {  // K/V loads of `tile`, whose entries are in *_cur
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int g = tid + j * NT;
       const int kk = g / CPR, c = g % CPR;
-      const int slot = kk / BK, r = kk % BK;
-      const int e = tile * SPT + slot;
-      int blk = -1;
-      if constexpr (DENSE) blk = e;
-      else if (e < nblk) blk = lidx[e];
+      const int r = kk % BK;
+      const int e = tile * SPT + kk / BK;
+      const int blk = DENSE ? e : (e < nblk ? nb_cur[j] : -1);
       const int key = blk * BK + r;
       const bool ok = DENSE ? key < a.L : (blk >= 0 && blk < a.NK && key < a.L);
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        kv4 = *reinterpret_cast<const uint4*>(kh + (size_t)key * D + c * 8);
-        vv4 = *reinterpret_cast<const uint4*>(vh + (size_t)key * D + c * 8);
-      }
-      kreg[j] = kv4;
-      vreg[j] = vv4;
+      const size_t off = (size_t)(ok ? key : 0) * D + c * 8;
+      kreg[j] = *reinterpret_cast<const u32x4*>(kh + off);
+      vreg[j] = *reinterpret_cast<const u32x4*>(vh + off);
     }
     if (tid < 64) {
-      const int kk = tid, slot = kk / BK, r = kk % BK;
-      const int e = tile * SPT + slot;
-      float b = -INFINITY;
-      bool slot_ok = false;
-      int key = 0;
-      if constexpr (DENSE) {
-        slot_ok = true;
-        key = e * BK + r;
-        if (key < a.L) b = 0.f;
-      } else if (e < nblk) {
-        const int blk = lidx[e];
-        slot_ok = blk >= 0 && blk < a.NK;
-        key = blk * BK + r;
-        if (slot_ok && key < a.L) b = __log2f(lw[e]);
-      }
-      bias_reg = b;
+      const int e = tile * SPT + tid / BK;
+      const int blk = DENSE ? e : (e < nblk ? nbb_cur : -1);
+      const int key = blk * BK + tid % BK;
+      const bool slot_ok = DENSE ? true : (blk >= 0 && blk < a.NK);
+      bias_reg = (slot_ok && key < a.L) ? (DENSE ? 0.f : __log2f(nbw_cur)) : -INFINITY;
       tail_reg = slot_ok && key >= a.L;  // a key past L inside a listed block
     }
   };
@@ -152,8 +169,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
     for (int j = 0; j < NCH; ++j) {
       const int g = tid + j * NT;
       const int kk = g / CPR, c = g % CPR;
-      *reinterpret_cast<uint4*>(&k_lds[buf][k_off<D>(kk, c)]) = kreg[j];
-      *reinterpret_cast<uint4*>(&v_lds[buf][v_off<D>(kk, c)]) = vreg[j];
+      *reinterpret_cast<u32x4*>(&k_lds[buf][k_off<D>(kk, c)]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&v_lds[buf][v_off<D>(kk, c)]) = vreg[j];
     }
     if (wid == 0) {
       bias_lds[buf][lane] = bias_reg;
@@ -188,14 +205,19 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
   ones[1] = (__bf16)1.f;
 
   if (ntiles > 0) {
+    fetch_idx(0);
+    rotate_idx();
+    if (ntiles > 1) fetch_idx(1);
     gather(0);
     stash(0);
+    rotate_idx();
   }
 #pragma unroll 1
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     __syncthreads();  // tile is in buf; every wave is done with buf ^ 1
-    if (tile + 1 < ntiles) gather(tile + 1);
+    if (tile + 2 < ntiles) fetch_idx(tile + 2);  // list entries of tile + 2 (first)
+    if (tile + 1 < ntiles) gather(tile + 1);     // K/V of tile + 1
     const unsigned char* kb = k_lds[buf];
     const unsigned char* vb = v_lds[buf];
 
@@ -292,6 +314,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
       }
     }
     if (tile + 1 < ntiles) stash(buf ^ 1);
+    rotate_idx();
   }
 
   // ---- epilogue: O = O^T / l, valid queries only
@@ -324,8 +347,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_kernel(AttendLaunch a) {
 // ============================================================================= launchers
 template <int D, int BQ, int BK, bool DENSE>
 static hipError_t launch_t(const AttendLaunch& a, hipStream_t st) {
-  const int nper = (a.rows + 7) / 8;
-  dim3 grid(nper * 8);
+  dim3 grid(a.rows);
   if (a.out_bf16)
     attend_kernel<D, BQ, BK, DENSE, true><<<grid, BQ * 2, 0, st>>>(a);
   else
