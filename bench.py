@@ -35,9 +35,26 @@ def parse():
     ap.add_argument("--kv-block", type=int, default=16)
     ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=640)
+    ap.add_argument("--cpu-sample-rows", type=int, default=1920)
     ap.add_argument("--extra", action="store_true", help="also time dense and top-k ablations")
     return ap.parse_args()
+
+
+def measured_traffic(workload_tag="wan14b_720p"):
+    """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if
+    it was taken on the current kernel source (else None: the kernel changed since)."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", f"attend_kernel_{workload_tag}_traffic.md")
+    src = os.path.join(ROOT, "block_sparse_attention_34_amd", "csrc", "absa_attend.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line
+                      and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "attend_source_sha256_16"))
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if fields.get("attend_source_sha256_16") == cur:
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def cpu_baseline(wl, keep, kv_block, nrows):
@@ -164,7 +181,9 @@ def main():
                    "q_block": Bq, "kv_block": Bk, "keep": args.keep, "clusters": 4, "kmeans_steps": 3,
                    "selection": "IBCS + SIP", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic() if (Bk == 16 and p.H == 40 and
+                                                       abs(args.keep - 0.095) < 1e-9) else None},
         "attend_ms": att_avg,
         "select_ms": sel_avg,
         "attend_dense_equiv_tflops": dense_flops / (att_avg * 1e-3) / 1e12,

@@ -62,11 +62,17 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   __shared__ __attribute__((aligned(16))) float bias_lds[2][64];
   __shared__ int tail_lds[2];
 
-  // Rows in order: consecutive workgroups (dispatched round-robin over the 8
-  // XCDs) take consecutive query blocks of one head, so all XCDs work on the
-  // same head's K/V at a time and it stays resident in the shared last-level
-  // cache (one head of the 720p workload is 39 MB; eight heads would not fit).
-  const int row = blockIdx.x;
+  // Row order.  Workgroups are dealt round-robin over the 8 XCDs, so a run of
+  // 8*64 consecutive workgroups covers ~one head's worth of rows that all share
+  // that head's K/V in the last-level cache.  Within such a group, XCD x takes
+  // the 64 adjacent query blocks [64x, 64x+64): neighbouring query blocks of a
+  // video select overlapping KV blocks, which then hit in that XCD's L2.
+  int row = blockIdx.x;
+  {
+    constexpr int R = 64, S = 8 * R;
+    const int g = row / S, i = row % S;
+    if ((g + 1) * S <= a.rows) row = g * S + (i & 7) * R + (i >> 3);
+  }
   if (row >= a.rows) return;
   const int bh = row / a.NQ, qb = row % a.NQ;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
