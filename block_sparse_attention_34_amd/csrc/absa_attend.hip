@@ -6,17 +6,21 @@
 //
 // One workgroup owns one row (b, h, query block): BQ/32 waves, each holding 32
 // queries.  The row's KV blocks are gathered 64 keys at a time (64/BK list
-// entries per tile) from HBM into LDS.  Per tile and wave:
+// entries per tile) from HBM straight into LDS.  Per tile and wave:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = the
 //                 wave's queries, kept in registers for the whole row);
 //   t = S * scale*log2(e) + log2(w_b)   (w_b the block's weight; -inf for
 //                 keys outside the list or past L);
 //   online max / exp2 / row sums per query (fp32), P rounded to bf16;
-//   O^T += V^T P^T on the same MFMA (A = V^T tile from LDS, B = P^T straight
+//   O^T += V^T P^T on the same MFMA (A = V^T read transposed from the
+//                 row-major V tile with ds_read_b64_tr_b16, B = P^T straight
 //                 from the S^T accumulators: the accumulator layout of the
 //                 first product is the operand layout of the second).
 // With queries in the N position of both products, each lane owns one query,
-// so the softmax statistics and the O^T rescale stay in-lane.
+// so the softmax statistics and the O^T rescale stay in-lane.  The tiles of
+// tile n+1 load while tile n computes (two LDS slots, one barrier per tile).
+#include <type_traits>
+
 #include "absa_device.h"
 #include "absa_launch.h"
 
@@ -44,29 +48,34 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a first-class vector, kept in VGPRs
 
+// K and V tiles arrive by direct global->LDS loads (global_load_lds_dwordx4:
+// lane l of a wave writes LDS base + 16 l), so no registers or LDS-store
+// instructions stage them; the row swizzle is applied by choosing which global
+// chunk each lane fetches.  The tile loop is unrolled by two so both ring slots
+// are distinct static LDS arrays.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 template <int D, int BQ, int BK, bool DENSE, bool OUT_BF16>
 __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLaunch a) {
-  constexpr int NT = BQ * 2;           // BQ/32 waves of 64 lanes
+  constexpr int NT = BQ * 2;           // threads
+  constexpr int NW = BQ / 32;          // waves, 32 queries each
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
-  constexpr int NCH = 64 * CPR / NT;   // chunks per thread per tile (K and V each)
+  constexpr int KPI = 64 / CPR;        // key rows covered by one wave-wide 16-byte load
+  constexpr int NCH = 64 * CPR / NT;   // wave-wide loads per thread per tile and tensor
   constexpr int SPT = 64 / BK;         // list entries per 64-key tile
   constexpr int KS = D / 16;           // k-steps of the QK product
   constexpr int DB = D / 32;           // 32-wide d blocks of O
-  constexpr int TILE = 64 * D * 2;     // bytes of one K or V tile
-  // Rescale threshold (log2 units): the running max is only moved when a
-  // tile's max exceeds it by more than this, so P stays <= 2^8.
+  constexpr int TILE = 64 * D * 2;
   constexpr float TAU = 8.f;
 
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][TILE];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][TILE];
-  __shared__ __attribute__((aligned(16))) float bias_lds[2][64];
-  __shared__ int tail_lds[2];
+  __shared__ __attribute__((aligned(16))) unsigned char k_s0[TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char k_s1[TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s0[TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s1[TILE];
+  __shared__ __attribute__((aligned(16))) float bias_s[2][64];
+  __shared__ int tail_s[2];
 
-  // Row order.  Workgroups are dealt round-robin over the 8 XCDs, so a run of
-  // 8*64 consecutive workgroups covers ~one head's worth of rows that all share
-  // that head's K/V in the last-level cache.  Within such a group, XCD x takes
-  // the 64 adjacent query blocks [64x, 64x+64): neighbouring query blocks of a
-  // video select overlapping KV blocks, which then hit in that XCD's L2.
   int row = blockIdx.x;
   {
     constexpr int R = 64, S = 8 * R;
@@ -75,119 +84,119 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   }
   if (row >= a.rows) return;
   const int bh = row / a.NQ, qb = row % a.NQ;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, qn = lane & 31;
   const size_t head_off = (size_t)bh * a.L * D;
   const uint16_t* __restrict__ kh = a.k + head_off;
   const uint16_t* __restrict__ vh = a.v + head_off;
 
-  // ---- this lane's query, as the B operand of S^T = K Q^T
   const int qi = qb * BQ + wid * 32 + qn;
   bf16x8 qf[KS];
   {
     const bool qv = qi < a.L;
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + head_off + (size_t)(qv ? qi : 0) * D);
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + head_off + (size_t)(qv ? qi : 0) * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 w = qp[2 * ks + h];
-      if (!qv) w = make_uint4(0, 0, 0, 0);
+      u32x4 w = qp[2 * ks + h];
+      if (!qv) w = u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  // ---- the row's list
-  int nblk, ntiles;
+  int nblk, T;
   const int32_t* lidx = nullptr;
   const float* lw = nullptr;
   if constexpr (DENSE) {
     nblk = (a.L + BK - 1) / BK;
-    ntiles = (a.L + 63) / 64;
+    T = (a.L + 63) / 64;
   } else {
     nblk = a.count[row];
     nblk = nblk < 0 ? 0 : (nblk > a.cap ? a.cap : nblk);
-    ntiles = (nblk + SPT - 1) / SPT;
+    T = (nblk + SPT - 1) / SPT;
     lidx = a.kv_idx + (size_t)row * a.cap;
     lw = a.inv_pi + (size_t)row * a.cap;
   }
+  if (T == 0) {
+    // empty list: the estimate is 0
+    if (qi < a.L) {
+#pragma unroll
+      for (int c = 0; c < D; c += 4) {
+        if constexpr (OUT_BF16)
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o) + head_off + (size_t)qi * D + c) =
+              make_uint2(0, 0);
+        else
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + head_off + (size_t)qi * D + c) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
 
-  // ---- gather of one tile into registers, and their store into an LDS buffer.
-  // The list entries a tile needs are fetched one iteration before its K/V
-  // loads are issued, so no K/V load waits on a list load.  K/V loads are
-  // unconditional: a masked key reads row 0 of the head (in bounds, finite) and
-  // its -inf bias removes it from the softmax.
-  // Raw list entries: *_cur for the tile whose K/V loads are issued next,
-  // *_nxt for the one after.  The loads of *_nxt are issued before the K/V loads
-  // and only read an iteration later (memory waits retire in issue order, so a
-  // list load issued after the K/V loads would hold them up).
-  int nb_cur[NCH], nb_nxt[NCH];
-  int nbb_cur = 0, nbb_nxt = 0;        // threads 0..63: block of key `tid`
-  float nbw_cur = 1.f, nbw_nxt = 1.f;  // and its weight
-  auto fetch_idx = [&](int tile) {     // raw entries of `tile` into *_nxt
+  // ---- list entries.  A wave-wide direct load covers KPI (<= BK) consecutive
+  // key rows, which lie in one block, so the entry it needs is wave-uniform.
+  // It is fetched with a vector load (a scalar load would share the LDS wait
+  // counter and, returning out of order, stall every LDS wait behind it) and
+  // made uniform when used.  Set F is fetched for tile n+3 during iteration n,
+  // used for K of n+3 in iteration n+1 and for V of n+3 in n+2.
+  static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
+  struct Entries {
+    int blk[NCH];  // wave-uniform block index of each wave-wide load
+    int bblk;      // threads 0..63: block of key `tid`
+    float bw;      //               and its weight
+  };
+  auto fetch = [&](Entries& E, int tile) {
     if constexpr (!DENSE) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int e = tile * SPT + ((tid + j * NT) / CPR) / BK;
+        const int kk = (j * NW + (tid >> 6)) * KPI + lane / CPR;  // same block for the whole wave
+        const int e = tile * SPT + kk / BK;
         const int ec = e < nblk ? e : nblk - 1;
-        nb_nxt[j] = lidx[ec < 0 ? 0 : ec];
+        E.blk[j] = lidx[ec];
       }
       if (tid < 64) {
         const int e = tile * SPT + tid / BK;
         const int ec = e < nblk ? e : nblk - 1;
-        nbb_nxt = lidx[ec < 0 ? 0 : ec];
-        nbw_nxt = lw[ec < 0 ? 0 : ec];
+        E.bblk = lidx[ec];
+        E.bw = lw[ec];
       }
     }
   };
-  auto rotate_idx = [&]() {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) nb_cur[j] = nb_nxt[j];
-    nbb_cur = nbb_nxt;
-    nbw_cur = nbw_nxt;
-  };
-  u32x4 kreg[NCH], vreg[NCH];
-  float bias_reg = -INFINITY;
-  bool tail_reg = false;
-  auto gather = [&](int tile) {  // K/V loads of `tile`, whose entries are in *_cur
+  // wave-wide direct loads of one tile of K or V (SWZ: 0 = K layout, 1 = V layout)
+  auto dma = [&](const uint16_t* __restrict__ src, unsigned char* buf, const Entries& E, int tile,
+                 auto SWZ) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int g = tid + j * NT;
-      const int kk = g / CPR, c = g % CPR;
-      const int r = kk % BK;
-      const int e = tile * SPT + kk / BK;
-      const int blk = DENSE ? e : (e < nblk ? nb_cur[j] : -1);
-      const int key = blk * BK + r;
-      const bool ok = DENSE ? key < a.L : (blk >= 0 && blk < a.NK && key < a.L);
-      const size_t off = (size_t)(ok ? key : 0) * D + c * 8;
-      kreg[j] = *reinterpret_cast<const u32x4*>(kh + off);
-      vreg[j] = *reinterpret_cast<const u32x4*>(vh + off);
+      const int ii = j * NW + wid;                 // wave-wide load index: LDS positions [64 ii, 64 ii + 64)
+      const int kk = ii * KPI + lane / CPR;        // key row of this lane's position
+      const int cp = lane % CPR;                   // chunk position within the row
+      int c;
+      if constexpr (decltype(SWZ)::value == 0) c = (D == 128) ? (cp ^ (kk & 15)) : (cp ^ ((kk >> 1) & 7));
+      else c = (D == 128) ? (cp ^ ((kk & 7) << 1)) : (cp ^ ((kk & 3) << 1));
+      const int e = tile * SPT + (ii * KPI) / BK;
+      int blk;
+      if constexpr (DENSE) blk = e;
+      else blk = e < nblk ? __builtin_amdgcn_readfirstlane(E.blk[j]) : -1;
+      const bool blk_ok = DENSE ? true : (blk >= 0 && blk < a.NK);
+      const int key = blk * BK + kk % BK;
+      const bool ok = blk_ok && key < a.L;
+      const uint16_t* g = src + (size_t)(ok ? key : 0) * D + c * 8;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(buf + ii * 1024), 16, 0, 0);
     }
+  };
+  auto put_bias = [&](int slot, const Entries& E, int tile) {
     if (tid < 64) {
       const int e = tile * SPT + tid / BK;
-      const int blk = DENSE ? e : (e < nblk ? nbb_cur : -1);
+      const int blk = DENSE ? e : (e < nblk ? E.bblk : -1);
       const int key = blk * BK + tid % BK;
       const bool slot_ok = DENSE ? true : (blk >= 0 && blk < a.NK);
-      bias_reg = (slot_ok && key < a.L) ? (DENSE ? 0.f : __log2f(nbw_cur)) : -INFINITY;
-      tail_reg = slot_ok && key >= a.L;  // a key past L inside a listed block
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int g = tid + j * NT;
-      const int kk = g / CPR, c = g % CPR;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][k_off<D>(kk, c)]) = kreg[j];
-      *reinterpret_cast<u32x4*>(&v_lds[buf][v_off<D>(kk, c)]) = vreg[j];
-    }
-    if (wid == 0) {
-      bias_lds[buf][lane] = bias_reg;
-      const unsigned long long any_tail = __ballot(tail_reg);
-      if (lane == 0) tail_lds[buf] = any_tail != 0ull;
+      bias_s[slot][tid] = (slot_ok && key < a.L) ? (DENSE ? 0.f : __log2f(E.bw)) : -INFINITY;
+      const unsigned long long any_tail = __ballot(slot_ok && key >= a.L);
+      if (lane == 0) tail_s[slot] = any_tail != 0ull;
     }
   };
 
-  // ---- per-lane offsets of the transposing V reads (see v_off): 16-lane group
-  // G, lane s in it; source row 4h + s/4 (+16 ks + 8 j), columns 32 db + 16 (G&1)
-  // + 4 (s&3) .. +3.
+  // V^T transposing-read offsets (see v_off)
   int voff[DB];
   {
     const int G = lane >> 4, s = lane & 15;
@@ -198,6 +207,9 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       voff[db] = v_off<D>(r0, col >> 3) + (col & 7) * 2;
     }
   }
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = k_off<D>(qn, 2 * ks + h);  // rows qn and 32 + qn share it
 
   f32x16 acc[DB];
 #pragma unroll
@@ -210,67 +222,54 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
 
-  if (ntiles > 0) {
-    fetch_idx(0);
-    rotate_idx();
-    if (ntiles > 1) fetch_idx(1);
-    gather(0);
-    stash(0);
-    rotate_idx();
-  }
-#pragma unroll 1
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    __syncthreads();  // tile is in buf; every wave is done with buf ^ 1
-    if (tile + 2 < ntiles) fetch_idx(tile + 2);  // list entries of tile + 2 (first)
-    if (tile + 1 < ntiles) gather(tile + 1);     // K/V of tile + 1
-    const unsigned char* kb = k_lds[buf];
-    const unsigned char* vb = v_lds[buf];
-
-    // S^T for 64 keys (two 32-key halves) x this wave's 32 queries
-    f32x16 sacc[2];
+  auto qk = [&](const unsigned char* kb, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
-      const int kk = sb * 32 + qn;  // A-operand row (key) of this lane
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + k_off<D>(kk, 2 * ks + h));
+        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + sb * 32 * (D * 2) + koff[ks]);
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], sacc[sb], 0, 0, 0);
       }
     }
-    // Lane (h, qn) register r of half sb holds key 32 sb + 8 (r/4) + 4 h + r%4.
-    // t = S scale log2(e) + log2(w_block) - m, with m the running reference.
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  // Logits of one tile: t = S scale log2(e) + log2(w) - m, with the bias read
+  // once per 4-key group (a group always lies in one block).  Returns this
+  // lane's max.  Branch-free, so it schedules together with the next tile's QK.
+  auto logits = [&](f32x16 (&sacc)[2], int slot, float m_use) {
     float mt = -INFINITY;
-    if (!tail_lds[buf]) {
-      // every 4-key group lies in one block and is all valid or all masked
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float cg = bias_lds[buf][32 * sb + 8 * g4 + 4 * h] - m_use;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float cg = bias_s[slot][32 * sb + 8 * g4 + 4 * h] - m_use;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float tv = fmaf(sacc[sb][4 * g4 + i], sl2, cg);
-            sacc[sb][4 * g4 + i] = tv;
-            mt = fmaxf(mt, tv);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float tv = fmaf(sacc[sb][r], sl2, bias_lds[buf][kk] - m_use);
-          sacc[sb][r] = tv;
+        for (int i = 0; i < 4; ++i) {
+          const float tv = fmaf(sacc[sb][4 * g4 + i], sl2, cg);
+          sacc[sb][4 * g4 + i] = tv;
           mt = fmaxf(mt, tv);
         }
-    }
+      }
+    return mt;
+  };
+  // Tiles holding keys past L inside a listed block (at most one per row):
+  // mask those keys individually and recompute the max.
+  auto mask_tail = [&](f32x16 (&sacc)[2], int slot) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (bias_s[slot][kk] == -INFINITY) sacc[sb][r] = -INFINITY;
+        mt = fmaxf(mt, sacc[sb][r]);
+      }
+    return mt;
+  };
+  // Rest of the softmax: move the reference if needed, P = 2^t in bf16, row sum.
+  auto finish_softmax = [&](f32x16 (&sacc)[2], float mt, float m_use, bf16x8 (&pf)[4]) {
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // Move the reference only when needed (first valid tile, or growth > TAU).
     if (mt > TAU || (m_run == -INFINITY && mt > -INFINITY)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-mt);
       l_run *= alpha;
@@ -284,8 +283,6 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[sb][r] -= mt;
     }
-    // P = 2^t rounded to bf16; the row sum adds exactly these rounded values
-    bf16x8 pf[4];
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -301,29 +298,74 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
           pf[sb * 2 + half][e + 1] = pk[1];
         }
     l_run += psum;
-
-    // O^T += V^T P^T: k-step ks covers keys 16 ks .. 16 ks + 15; this lane's 8
-    // keys are 16 ks + {4h..4h+3} and 16 ks + 8 + {4h..4h+3}, matching pf[ks];
-    // the two transposing reads deliver exactly those keys for column 32 db + qn.
+  };
+  auto pv = [&](const unsigned char* vb, const bf16x8 (&pf)[4]) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
         const unsigned char* p0 = vb + voff[db] + (16 * ks) * (D * 2);
-        const unsigned char* p1 = p0 + 8 * (D * 2);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * (D * 2)));
         const i16x4 w[2] = {lo, hi};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks],
                                                           acc[db], 0, 0, 0);
       }
     }
-    if (tile + 1 < ntiles) stash(buf ^ 1);
-    rotate_idx();
+  };
+  auto wait_dma_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
+    __syncthreads();
+  };
+
+  // ---- schedule: slot p = n % 2 holds K, V and bias of tile n; the direct
+  // loads of tile n+1 into slot p^1 are issued before the compute of tile n
+  // and waited for at its end, followed by one barrier.
+  auto uniformize = [&](Entries& E) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) E.blk[j] = __builtin_amdgcn_readfirstlane(E.blk[j]);
+  };
+  Entries EC, EF;  // EC: entries of the tile whose loads are issued next; EF: being fetched
+  fetch(EC, 0);
+  if (T > 1) fetch(EF, 1);
+  uniformize(EC);
+  dma(kh, k_s0, EC, 0, std::integral_constant<int, 0>{});
+  dma(vh, v_s0, EC, 0, std::integral_constant<int, 1>{});
+  put_bias(0, EC, 0);
+  wait_dma_and_sync();
+  EC = EF;
+  uniformize(EC);
+  auto iteration = [&](int n, auto PAR) {
+    constexpr int p = decltype(PAR)::value;
+    unsigned char* k_cur = p ? k_s1 : k_s0;
+    unsigned char* v_cur = p ? v_s1 : v_s0;
+    unsigned char* k_nxt = p ? k_s0 : k_s1;
+    unsigned char* v_nxt = p ? v_s0 : v_s1;
+    if (n + 2 < T) fetch(EF, n + 2);
+    if (n + 1 < T) {
+      dma(kh, k_nxt, EC, n + 1, std::integral_constant<int, 0>{});
+      dma(vh, v_nxt, EC, n + 1, std::integral_constant<int, 1>{});
+      put_bias(p ^ 1, EC, n + 1);
+    }
+    f32x16 sacc[2];
+    qk(k_cur, sacc);
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float mt = logits(sacc, p, m_use);
+    if (tail_s[p]) mt = mask_tail(sacc, p);
+    bf16x8 pf[4];
+    finish_softmax(sacc, mt, m_use, pf);
+    pv(v_cur, pf);
+    wait_dma_and_sync();
+    EC = EF;
+    uniformize(EC);
+  };
+#pragma unroll 1
+  for (int n = 0; n < T; n += 2) {
+    iteration(n, std::integral_constant<int, 0>{});
+    if (n + 1 < T) iteration(n + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- epilogue: O = O^T / l, valid queries only
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qi < a.L) {
