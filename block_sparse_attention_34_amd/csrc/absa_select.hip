@@ -83,133 +83,180 @@ __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __re
 // Lloyd k-means of one query block (one workgroup per row).  Queries stay in
 // token order; centroids start at members floor(j n / C); each step assigns
 // every query to its nearest centroid (squared Euclidean, ties to the lowest
-// j) and moves each non-empty centroid to the mean of its members.
+// j) and moves each non-empty centroid to the mean of its members.  Both
+// contractions run on v_mfma_f32_32x32x16_bf16:
+//  * assignment: G[j][q] = mu_j . x_q with the centroids split into bf16 high
+//    and low parts (two products; exact for centroids representable in 16
+//    significant bits, within 2^-17 relative otherwise); the nearest centroid
+//    minimises |mu_j|^2 - 2 G[j][q] (|x|^2 is common to all j), ties to the
+//    lowest j;
+//  * update: sums[j][c] = sum_q [a(q) = j] x_q[c] as a product of a 0/1
+//    assignment matrix with the query block (exact products, fp32 sums), then
+//    one correctly rounded division by n_j.
 template <int D>
-__global__ __launch_bounds__(256) void ibcs_kmeans_kernel(const uint16_t* __restrict__ q,
-                                                          float* __restrict__ mu_out,
-                                                          int* __restrict__ nj_out, int L, int Bq,
-                                                          int NQ, int C, int Tk) {
-  constexpr int XS = D / 2 + 1;  // row stride in dwords (bf16 pairs), odd -> conflict-free
-  constexpr int G = 256 / D;     // query groups in the update step
-  __shared__ uint32_t X[128 * XS];
-  __shared__ float mu[8][D];
-  __shared__ float dpart[2][128][8];
-  __shared__ float upd[G][8][D];
-  __shared__ int label[128];
-  __shared__ int cnt[8];
+__device__ __forceinline__ int xq_off(int q, int c) {  // byte offset of 16-byte chunk c of query row q
+  if constexpr (D == 128) return q * 256 + ((c ^ (q & 15)) << 4);
+  else return q * 128 + ((c ^ ((q >> 1) & 7)) << 4);
+}
 
-  const int t = threadIdx.x;
+template <int D, int C>
+__global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* __restrict__ q,
+                                                               float* __restrict__ mu_out,
+                                                               int* __restrict__ nj_out, int L, int Bq,
+                                                               int NQ, int Tk) {
+  constexpr int KS = D / 16;   // k-steps of the assignment product
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int NB = D / 32;   // 32-wide column blocks of the update product
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  __shared__ __attribute__((aligned(16))) unsigned char xs[128 * D * 2];
+  __shared__ float mu_s[C][D];
+  __shared__ __attribute__((aligned(16))) __bf16 mu_hi[C][D], mu_lo[C][D];
+  __shared__ float musq[C];
+  __shared__ __attribute__((aligned(16))) int lab[128];
+  __shared__ int cnt[C];
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h = lane >> 5, nn = lane & 31;
   const int row = blockIdx.x;
   const int bh = row / NQ, i = row % NQ;
   const int q0 = i * Bq;
   const int n = min(Bq, L - q0);
+
+  // query block -> LDS (rows >= n are zero)
   {
-    // 128 x D bf16 = 128 x D/8 16-byte chunks; every load is issued before any store
-    constexpr int CH = D / 8, PER = 128 * CH / 256;
-    const uint4* src = reinterpret_cast<const uint4*>(q + ((size_t)bh * L + q0) * D);
-    uint4 wv[PER];
+    constexpr int PER = 128 * CH / 256;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)bh * L + q0) * D);
+    u32x4 wv[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int idx = t + 256 * j;
-      wv[j] = (idx / CH < n) ? src[idx] : make_uint4(0, 0, 0, 0);
+      wv[j] = (idx / CH < n) ? src[idx] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int idx = t + 256 * j;
-      const int qq = idx / CH, cp = (idx % CH) * 4;
-      if (qq < n) {
-        X[qq * XS + cp + 0] = wv[j].x;
-        X[qq * XS + cp + 1] = wv[j].y;
-        X[qq * XS + cp + 2] = wv[j].z;
-        X[qq * XS + cp + 3] = wv[j].w;
-      }
+      *reinterpret_cast<u32x4*>(xs + xq_off<D>(idx / CH, idx % CH)) = wv[j];
     }
   }
   __syncthreads();
   for (int idx = t; idx < C * D; idx += 256) {
     const int j = idx / D, c = idx % D;
     const int m = (j * n) / C;
-    const uint32_t w = X[m * XS + (c >> 1)];
-    mu[j][c] = (c & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    const uint16_t bits = *reinterpret_cast<const uint16_t*>(xs + xq_off<D>(m, c >> 3) + (c & 7) * 2);
+    mu_s[j][c] = __uint_as_float((uint32_t)bits << 16);
   }
   __syncthreads();
 
 #pragma unroll 1
   for (int step = 0; step < Tk; ++step) {
-    // assign: thread -> (query qq, half hf of the dims)
-    {
-      const int qq = t & 127, hf = t >> 7;
-      if (qq < n) {
-        float dist[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dist[j] = 0.f;
-        const uint32_t* xr = X + qq * XS + hf * (D / 4);
-#pragma unroll 4
-        for (int cp = 0; cp < D / 4; ++cp) {
-          float x0, x1;
-          unpack_bf16x2(xr[cp], x0, x1);
-          const int c = hf * (D / 2) + 2 * cp;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (j < C) {
-              const float d0 = x0 - mu[j][c], d1 = x1 - mu[j][c + 1];
-              dist[j] = fmaf(d0, d0, dist[j]);
-              dist[j] = fmaf(d1, d1, dist[j]);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < C) dpart[hf][qq][j] = dist[j];
-      }
-    }
-    if (t < 8) cnt[t] = 0;
-    __syncthreads();
-    if (t < n) {
-      int best = 0;
-      float bd = dpart[0][t][0] + dpart[1][t][0];
-      for (int j = 1; j < C; ++j) {
-        const float dj = dpart[0][t][j] + dpart[1][t][j];
-        if (dj < bd) { bd = dj; best = j; }
-      }
-      label[t] = best;
-      atomicAdd(&cnt[best], 1);
-    }
-    __syncthreads();
-    // update: thread -> (group g of queries, dim c)
-    {
-      const int c = t % D, g = t / D;
-      const int per = (n + G - 1) / G;
-      const int qa = g * per, qb = min(n, qa + per);
-      float sum[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sum[j] = 0.f;
-      for (int qq = qa; qq < qb; ++qq) {
-        const uint32_t w = X[qq * XS + (c >> 1)];
-        const float x = (c & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
-        const int lb = label[qq];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j == lb) sum[j] += x;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) upd[g][j][c] = sum[j];
-    }
-    __syncthreads();
+    // ---- split the centroids into bf16 parts, and |mu_j|^2
     for (int idx = t; idx < C * D; idx += 256) {
       const int j = idx / D, c = idx % D;
-      if (cnt[j] > 0) {
-        float s = 0.f;
+      const float m = mu_s[j][c];
+      const __bf16 hi = (__bf16)m;
+      mu_hi[j][c] = hi;
+      mu_lo[j][c] = (__bf16)(m - (float)hi);
+    }
+    if (t < C) cnt[t] = 0;
+    if (w < C) {  // wave w: |mu_w|^2 (fixed order: lane partial sums, then the wave sum)
+      float sq = 0.f;
+      for (int c = lane; c < D; c += 64) sq = fmaf(mu_s[w][c], mu_s[w][c], sq);
+      sq = wave_sum(sq);
+      if (lane == 0) musq[w] = sq;
+    }
+    if (C > 4 && w < C - 4) {
+      float sq = 0.f;
+      for (int c = lane; c < D; c += 64) sq = fmaf(mu_s[w + 4][c], mu_s[w + 4][c], sq);
+      sq = wave_sum(sq);
+      if (lane == 0) musq[w + 4] = sq;
+    }
+    __syncthreads();
+    // ---- assignment: wave w owns queries 32 w .. 32 w + 31
+    if (32 * w < n) {
+      f32x16 g;
 #pragma unroll
-        for (int g = 0; g < G; ++g) s += upd[g][j][c];
-        mu[j][c] = __fdiv_rn(s, (float)cnt[j]);
+      for (int r = 0; r < 16; ++r) g[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xs + xq_off<D>(32 * w + nn, 2 * ks + h));
+        bf16x8 ah, al;
+        if (nn < C) {
+          ah = *reinterpret_cast<const bf16x8*>(&mu_hi[nn][16 * ks + 8 * h]);
+          al = *reinterpret_cast<const bf16x8*>(&mu_lo[nn][16 * ks + 8 * h]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { ah[e] = (__bf16)0.f; al[e] = (__bf16)0.f; }
+        }
+        g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb, g, 0, 0, 0);
+      }
+      // lane (h, nn) register r holds centroid 8 (r/4) + 4 h + r%4 for query 32 w + nn
+      float best = INFINITY;
+      int bj = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * h + r;
+        if (j < C) {
+          const float dj = musq[j] - 2.f * g[r];
+          if (dj < best) { best = dj; bj = j; }
+        }
+      }
+      if constexpr (C > 4) {
+        const float ob = __shfl_xor(best, 32, 64);
+        const int oj = __shfl_xor(bj, 32, 64);
+        if (ob < best || (ob == best && oj < bj)) { best = ob; bj = oj; }
+      }
+      const int qq = 32 * w + nn;
+      const bool valid = qq < n;
+      if (h == 0) lab[qq] = valid ? bj : -1;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const unsigned long long m = __ballot(h == 0 && valid && bj == j);
+        if (lane == 0 && m) atomicAdd(&cnt[j], (int)__popcll(m));
+      }
+    } else if (lane < 32) {
+      lab[32 * w + lane] = -1;
+    }
+    __syncthreads();
+    // ---- update: wave w owns columns 32 w .. 32 w + 31
+    if (w < NB) {
+      f32x16 sum;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {  // 16 queries per k-step
+        // A: 0/1 assignment of queries 16 ks + {4h..4h+3, 8+4h..8+4h+3} to centroid nn
+        const int4 la = *reinterpret_cast<const int4*>(&lab[16 * ks + 4 * h]);
+        const int4 lb = *reinterpret_cast<const int4*>(&lab[16 * ks + 8 + 4 * h]);
+        const int lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        bf16x8 oh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oh[e] = (__bf16)(lv[e] == nn ? 1.f : 0.f);
+        // B: the same queries' values in columns 32 w + (lane & 31), read transposed
+        const int G = lane >> 4, sl = lane & 15;
+        const int col = 32 * w + 16 * (G & 1) + 4 * (sl & 3);
+        const int qa = 16 * ks + 4 * h + (sl >> 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(xs + xq_off<D>(qa, col >> 3) + (col & 7) * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(xs + xq_off<D>(qa + 8, col >> 3) + (col & 7) * 2));
+        const i16x4 xv[2] = {lo, hi};
+        sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh, __builtin_bit_cast(bf16x8, xv), sum, 0, 0, 0);
+      }
+      // lane (h, nn) register r holds centroid 4 h + r (r < 4) for column 32 w + nn
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * h + r;
+        if (j < C && cnt[j] > 0) mu_s[j][32 * w + nn] = __fdiv_rn(sum[r], (float)cnt[j]);
       }
     }
     __syncthreads();
   }
   float* mo = mu_out + (size_t)row * C * D;
-  for (int idx = t; idx < C * D; idx += 256) mo[idx] = mu[idx / D][idx % D];
-  if (t < C) nj_out[(size_t)row * C + t] = (Tk > 0) ? cnt[t] : 0;
+  for (int idx = t; idx < C * D; idx += 256) mo[idx] = mu_s[idx / D][idx % D];
+  if (t < C) nj_out[(size_t)row * C + t] = cnt[t];
 }
 
 // ============================================================================= K2b
@@ -527,10 +574,24 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   }
   // K2a
   {
-    if (a.d == 128)
-      ibcs_kmeans_kernel<128><<<rows, 256, 0, st>>>(a.q, a.mu, a.nj, a.L, a.Bq, a.NQ, a.C, a.Tk);
-    else
-      ibcs_kmeans_kernel<64><<<rows, 256, 0, st>>>(a.q, a.mu, a.nj, a.L, a.Bq, a.NQ, a.C, a.Tk);
+#define ABSA_KM(DD, CC) \
+  ibcs_kmeans_mfma_kernel<DD, CC><<<rows, 256, 0, st>>>(a.q, a.mu, a.nj, a.L, a.Bq, a.NQ, a.Tk)
+    if (a.d == 128) {
+      switch (a.C) {
+        case 1: ABSA_KM(128, 1); break;
+        case 2: ABSA_KM(128, 2); break;
+        case 4: ABSA_KM(128, 4); break;
+        default: ABSA_KM(128, 8); break;
+      }
+    } else {
+      switch (a.C) {
+        case 1: ABSA_KM(64, 1); break;
+        case 2: ABSA_KM(64, 2); break;
+        case 4: ABSA_KM(64, 4); break;
+        default: ABSA_KM(64, 8); break;
+      }
+    }
+#undef ABSA_KM
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
