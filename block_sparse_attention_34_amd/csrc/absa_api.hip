@@ -70,7 +70,7 @@ absa_status check_params(const absa_problem* p, const absa_select_params* s, Sel
   return ABSA_OK;
 }
 
-constexpr int kWsRegions = 5;
+constexpr int kWsRegions = 6;  // the first 5 are published by absa_select_workspace_layout
 
 struct WsLayout {
   size_t off[kWsRegions];
@@ -90,6 +90,10 @@ WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
   o = align_up(o + (size_t)dm.rows * dm.NK * sizeof(float), kWsAlign);
   w.off[4] = o;
   o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
+  w.off[5] = o;
+  int per;
+  const int nsplit = absa::logit_splits(dm.NQ, C, (int)dm.BH, dm.NKp, &per);
+  o = align_up(o + (size_t)dm.rows * C * nsplit * 2 * sizeof(float), kWsAlign);
   w.total = o;
   return w;
 }
@@ -157,7 +161,7 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
   st = check_params(prob, params, &sp);
   if (st != ABSA_OK) return st;
   const WsLayout w = ws_layout(prob, dm, sp.C);
-  for (int i = 0; i < kWsRegions; ++i) offsets[i] = w.off[i];
+  for (int i = 0; i < 5; ++i) offsets[i] = w.off[i];
   return ABSA_OK;
 }
 
@@ -213,6 +217,7 @@ absa_status absa_select(const absa_problem* prob, const absa_select_params* para
   a.nj = reinterpret_cast<int*>(ws + w.off[2]);
   a.s = reinterpret_cast<float*>(ws + w.off[3]);
   a.logit = reinterpret_cast<float*>(ws + w.off[4]);
+  a.mz = reinterpret_cast<float2*>(ws + w.off[5]);
   a.count = out->count;
   a.kv_idx = out->kv_idx;
   a.inv_pi = out->inv_pi;

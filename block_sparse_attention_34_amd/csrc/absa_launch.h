@@ -17,6 +17,7 @@ struct SelectLaunch {
   int* nj;       // workspace: [rows][C]
   float* s;      // workspace: [rows][NK]
   float* logit;  // workspace: [rows][C][NK]
+  float2* mz;    // workspace: [rows][C][nsplit] per-split (max, normaliser) of each centroid
   int32_t* count;
   int32_t* kv_idx;
   float* inv_pi;
@@ -34,6 +35,18 @@ struct AttendLaunch {
   int L, d, Bq, Bk, NQ, NK, rows, cap, out_bf16;
   float scale_log2;  // softmax scale times log2(e)
 };
+
+// Number of block-range splits of the logit product (and the 32-block tiles per
+// split), chosen so the launch has at least ~2048 workgroups.
+inline int logit_splits(int NQ, int C, int BH, int NKp, int* tiles_per_split) {
+  const int mtiles = (NQ * C + 127) / 128;
+  const int ntile_all = NKp / 32;
+  int nsplit = (2048 + mtiles * BH - 1) / (mtiles * BH);
+  nsplit = nsplit < 1 ? 1 : (nsplit > ntile_all ? ntile_all : nsplit);
+  const int per = (ntile_all + nsplit - 1) / nsplit;
+  *tiles_per_split = per;
+  return (ntile_all + per - 1) / per;
+}
 
 hipError_t launch_select(const SelectLaunch& a, hipStream_t st);
 hipError_t configure_select_kernels();

@@ -13,12 +13,10 @@
 
 namespace absa {
 
-// 2^x, exact whenever the result is representable and x is an integer: the
-// integer part goes through ldexp, only the fractional part through v_exp_f32.
-__device__ __forceinline__ float exp2_split(float x) {
-  const float fl = floorf(x);
-  return ldexpf(__builtin_amdgcn_exp2f(x - fl), (int)fl);
-}
+// 2^x on v_exp_f32.  On gfx950 it returns the exact power of two at every
+// integer argument in [-126, 125] (checked on the device), and every argument
+// used here is >= -64, so inputs whose logits are integers give exact terms.
+__device__ __forceinline__ float exp2_split(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================================================================= K1
 // kbar^T[bh][c][b] = (1/n_b) sum_{valid keys of block b} K[bh][key][c].
@@ -269,8 +267,10 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
 template <int D>
 __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict__ kbarT,
                                                          const float* __restrict__ mu,
-                                                         float* __restrict__ logit, int M, int NK,
-                                                         int NKp, int tiles_per_split, float alpha) {
+                                                         float* __restrict__ logit,
+                                                         float2* __restrict__ mz, int M, int NK,
+                                                         int NKp, int L, int Bk, int tiles_per_split,
+                                                         float alpha) {
   constexpr int KS = D / 2;  // k-steps of 2 dims
   __shared__ __attribute__((aligned(16))) float kt[2][D * 32];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -291,25 +291,31 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
     for (int s2 = 0; s2 < KS; ++s2) areg[s2] = (m < M) ? src[2 * s2 + h] : 0.f;
   }
   const float* kb = kbarT + (size_t)bh * D * NKp;
-  float4 stage[D / 32];
+  typedef float f32v4 __attribute__((ext_vector_type(4)));  // kept in VGPRs
+  f32v4 stage[D / 32];
   auto fetch = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-      const int idx = t + 256 * i;  // float4 index in the [D][32] tile
+      const int idx = t + 256 * i;  // 16-byte index in the [D][32] tile
       const int c = idx >> 3, b4 = idx & 7;
-      stage[i] = *reinterpret_cast<const float4*>(kb + (size_t)c * NKp + tile * 32 + b4 * 4);
+      stage[i] = *reinterpret_cast<const f32v4*>(kb + (size_t)c * NKp + tile * 32 + b4 * 4);
     }
   };
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
       const int idx = t + 256 * i;
-      *reinterpret_cast<float4*>(&kt[buf][idx * 4]) = stage[i];
+      *reinterpret_cast<f32v4*>(&kt[buf][idx * 4]) = stage[i];
     }
   };
   fetch(tile0);
   put(0);
   float* out_base = logit + (size_t)bh * M * NK;
+  // running max m and normaliser Z = sum nk 2^(l - m) of the 16 centroids this
+  // lane sees (terms more than 64 octaves below the max dropped)
+  float rm[16], rz[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { rm[r] = -INFINITY; rz[r] = 0.f; }
 #pragma unroll 1
   for (int tile = tile0; tile < tile1; ++tile) {
     const int buf = (tile - tile0) & 1;
@@ -323,13 +329,38 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(areg[s2], kt[buf][(2 * s2 + h) * 32 + n], acc, 0, 0, 0);
     const int b = tile * 32 + n;
     if (b < NK) {
+      const float nk = (float)min(Bk, L - b * Bk);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) out_base[(size_t)m * NK + b] = alpha * acc[r];
+        const float l = alpha * acc[r];
+        if (m < M) out_base[(size_t)m * NK + b] = l;
+        const float mn = fmaxf(rm[r], l);
+        const float d0 = rm[r] - mn, d1 = l - mn;
+        const float e0 = d0 >= -64.f ? exp2_split(d0) : 0.f;
+        const float e1 = d1 >= -64.f ? exp2_split(d1) : 0.f;
+        rz[r] = fmaf(rz[r], e0, nk * e1);
+        rm[r] = mn;
       }
     }
     if (tile + 1 < tile1) put(buf ^ 1);
+  }
+  // combine over the 32 blocks (lanes) of each half-wave and write this split's
+  // partial (m, Z) of every centroid
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const float m2 = __shfl_xor(rm[r], o, 64), z2 = __shfl_xor(rz[r], o, 64);
+      const float mn = fmaxf(rm[r], m2);
+      const float d0 = rm[r] - mn, d1 = m2 - mn;
+      const float e0 = d0 >= -64.f ? exp2_split(d0) : 0.f;
+      const float e1 = d1 >= -64.f ? exp2_split(d1) : 0.f;
+      rz[r] = fmaf(rz[r], e0, z2 * e1);
+      rm[r] = mn;
+    }
+    const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (n == 0 && m < M) mz[((size_t)bh * M + m) * gridDim.z + blockIdx.z] = make_float2(rm[r], rz[r]);
   }
 }
 
@@ -340,6 +371,7 @@ constexpr int SIP_NT = 256;
 
 template <int C>
 __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ logit,
+                                                     const float2* __restrict__ mz, int nsplit,
                                                      const int* __restrict__ nj,
                                                      float* __restrict__ s_out, int L, int Bq, int Bk,
                                                      int NK, int NQ,
@@ -353,78 +385,36 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
   unsigned char* flag = reinterpret_cast<unsigned char*>(s + NK);  // [NK]
   __shared__ float redf[SIP_NT / 64];
   __shared__ int redi[SIP_NT / 64];
-  __shared__ float redm[C][SIP_NT / 64], redz[C][SIP_NT / 64];
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int t = threadIdx.x;
   const int row = blockIdx.x;
   const int bh = row / NQ, i = row % NQ;
 
   // ---- IBCS scores of this row from its logits: per centroid the max m_j and
   // the normaliser Z_j = sum_b nk_b 2^(l_jb - m_j) (terms below 2^-64 of the
-  // max dropped), then s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j.
+  // max dropped; combined from the logit kernel's per-split partials), then
+  // s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j.
   {
     const float* lrow = logit + (size_t)row * C * NK;
-    float mj[C], zj[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) { mj[j] = -INFINITY; zj[j] = 0.f; }
-    constexpr int U = 4;  // blocks per batch: U*C loads in flight
-#pragma unroll 1
-    for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
-      float lv[U][C];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const int b = b0 + u * SIP_NT;
-          lv[u][j] = (b < NK) ? lrow[(size_t)j * NK + b] : -INFINITY;
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int b = b0 + u * SIP_NT;
-        if (b >= NK) break;
-        const float nk = (float)min(Bk, L - b * Bk);
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const float l = lv[u][j];
-          if (l > mj[j]) {
-            zj[j] = (mj[j] - l >= -64.f) ? fmaf(zj[j], exp2_split(mj[j] - l), nk) : nk;
-            mj[j] = l;
-          } else if (l - mj[j] >= -64.f) {
-            zj[j] = fmaf(nk, exp2_split(l - mj[j]), zj[j]);
-          }
-        }
+    __shared__ float coef_s[C], mj_s[C];
+    if (t < C) {
+      const float2* pz = mz + ((size_t)row * C + t) * nsplit;
+      float m = -INFINITY;
+      for (int z = 0; z < nsplit; ++z) m = fmaxf(m, pz[z].x);
+      float zs = 0.f;
+      for (int z = 0; z < nsplit; ++z) {
+        const float d = pz[z].x - m;
+        if (d >= -64.f) zs = fmaf(pz[z].y, exp2_split(d), zs);
       }
-    }
-    // combine (m, Z) pairs: lanes, then waves
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float m2 = __shfl_xor(mj[j], o, 64), z2 = __shfl_xor(zj[j], o, 64);
-        const float m = fmaxf(mj[j], m2);
-        float z = 0.f;
-        if (mj[j] - m >= -64.f) z += zj[j] * exp2_split(mj[j] - m);
-        if (m2 - m >= -64.f) z += z2 * exp2_split(m2 - m);
-        mj[j] = m;
-        zj[j] = z;
-      }
-      if (lane == 0) { redm[j][wid] = mj[j]; redz[j][wid] = zj[j]; }
+      const int n = min(Bq, L - i * Bq);
+      const int cnt = nj[(size_t)row * C + t];
+      mj_s[t] = m;
+      coef_s[t] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), zs) : 0.f;
     }
     __syncthreads();
-    const int n = min(Bq, L - i * Bq);
-    float coef[C];
+    float mj[C], coef[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < SIP_NT / 64; ++w) m = fmaxf(m, redm[j][w]);
-      float z = 0.f;
-#pragma unroll
-      for (int w = 0; w < SIP_NT / 64; ++w)
-        if (redm[j][w] - m >= -64.f) z += redz[j][w] * exp2_split(redm[j][w] - m);
-      mj[j] = m;
-      const int cnt = nj[(size_t)row * C + j];
-      coef[j] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), z) : 0.f;
-    }
+    for (int j = 0; j < C; ++j) { mj[j] = mj_s[j]; coef[j] = coef_s[j]; }
+    constexpr int U = 4;  // blocks per batch: U*C loads in flight
     float* srow_out = s_out + (size_t)row * NK;
 #pragma unroll 1
     for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
@@ -599,24 +589,26 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   {
     const int M = a.NQ * a.C;
     const int mtiles = (M + 127) / 128;
-    const int ntile_all = a.NKp / 32;
-    int nsplit = (2048 + mtiles * BH - 1) / (mtiles * BH);
-    nsplit = nsplit < 1 ? 1 : (nsplit > ntile_all ? ntile_all : nsplit);
-    const int per = (ntile_all + nsplit - 1) / nsplit;
-    nsplit = (ntile_all + per - 1) / per;
+    int per;
+    const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
     dim3 grid(mtiles, BH, nsplit);
     if (a.d == 128)
-      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, M, a.NK, a.NKp, per, a.alpha);
+      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
+                                                   a.Bk, per, a.alpha);
     else
-      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, M, a.NK, a.NKp, per, a.alpha);
+      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
+                                                  a.Bk, per, a.alpha);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // K3
   {
+    int per;
+    const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
     const size_t lds = (size_t)a.NK * (sizeof(float) + 1);
 #define ABSA_SIP(CC)                                                                                  \
-  sip_kernel<CC><<<rows, SIP_NT, lds, st>>>(a.logit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK, a.NQ, a.nstar,  \
+  sip_kernel<CC><<<rows, SIP_NT, lds, st>>>(a.logit, a.mz, nsplit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK,  \
+                                            a.NQ, a.nstar,                                              \
                                             a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
                                             a.inv_pi, a.cap, a.pi_out)
     switch (a.C) {
