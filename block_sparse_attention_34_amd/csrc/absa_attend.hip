@@ -35,27 +35,35 @@ __device__ __forceinline__ int k_off(int kk, int c) {
   else return kk * 128 + ((c ^ ((kk >> 1) & 7)) << 4);
 }
 
-// V tile: chunk c of row kk at c ^ 2(kk & 7) (D = 128).  V is read with
-// ds_read_b64_tr_b16, where a 16-lane group reads 4 consecutive rows x 32
-// bytes; the even xor keeps those 8 chunks on distinct bank groups.
+// V tile: chunk c of row kk at c ^ 4 (kk & 3) (D = 128; D = 64: c ^ 4 ((kk >> 1) & 1)).
+// V is read with ds_read_b64_tr_b16: a half-wave reads 4 consecutive rows x 64
+// bytes (chunks 4 db .. 4 db + 3); the xor moves each row's four chunks to a
+// different quarter of the banks (for D = 64, rows of equal parity share a bank
+// half and the xor separates them).
 template <int D>
 __device__ __forceinline__ int v_off(int kk, int c) {
-  if constexpr (D == 128) return kk * 256 + ((c ^ ((kk & 7) << 1)) << 4);
-  else return kk * 128 + ((c ^ ((kk & 3) << 1)) << 4);
+  if constexpr (D == 128) return kk * 256 + ((c ^ ((kk & 3) << 2)) << 4);
+  else return kk * 128 + ((c ^ (((kk >> 1) & 1) << 2)) << 4);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a first-class vector, kept in VGPRs
 
-// K and V tiles arrive by direct global->LDS loads (global_load_lds_dwordx4:
-// lane l of a wave writes LDS base + 16 l), so no registers or LDS-store
-// instructions stage them; the row swizzle is applied by choosing which global
-// chunk each lane fetches.  The tile loop is unrolled by two so both ring slots
-// are distinct static LDS arrays.
+// K, V and the per-key bias have separate two-slot LDS rings; K and the bias
+// run one tile ahead of V.  Iteration n overlaps the two matrix products with
+// the vector work of the neighbouring tile:
+//   phase A: QK(n+1) on the matrix core  ||  2^t, bf16 rounding, row sum of tile n
+//   phase B: PV(n) on the matrix core    ||  logits t of tile n+1
+// then (rarely) the tail mask and the rescale of tile n+1, and one barrier.
+// Tiles arrive by direct buffer->LDS loads (buffer_load_dwordx4 ... lds: lane
+// l of a wave writes LDS base + 16 l); the row swizzle is applied by choosing
+// which chunk each lane fetches.  The loop is unrolled by two so every ring
+// slot is a distinct static LDS array.
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
+// Two workgroups of 256 threads per CU (at most 256 VGPRs per lane) hide the
+// barrier of one behind the matrix work of the other.
 template <int D, int BQ, int BK, bool DENSE, bool OUT_BF16>
 __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLaunch a) {
   constexpr int NT = BQ * 2;           // threads
@@ -67,7 +75,8 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   constexpr int KS = D / 16;           // k-steps of the QK product
   constexpr int DB = D / 32;           // 32-wide d blocks of O
   constexpr int TILE = 64 * D * 2;
-  constexpr float TAU = 8.f;
+  constexpr float TAU = 8.f;           // the running max moves only when exceeded by this
+  static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
 
   __shared__ __attribute__((aligned(16))) unsigned char k_s0[TILE];
   __shared__ __attribute__((aligned(16))) unsigned char k_s1[TILE];
@@ -76,6 +85,11 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   __shared__ __attribute__((aligned(16))) float bias_s[2][64];
   __shared__ int tail_s[2];
 
+  // Row order.  Workgroups are dealt round-robin over the 8 XCDs, so a run of
+  // 8*64 consecutive workgroups covers ~one head's worth of rows that all share
+  // that head's K/V in the last-level cache.  Within such a group, XCD x takes
+  // the 64 adjacent query blocks [64x, 64x+64): neighbouring query blocks of a
+  // video select overlapping KV blocks, which then hit in that XCD's L2.
   int row = blockIdx.x;
   {
     constexpr int R = 64, S = 8 * R;
@@ -88,9 +102,8 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, qn = lane & 31;
   const size_t head_off = (size_t)bh * a.L * D;
-  const uint16_t* __restrict__ kh = a.k + head_off;
-  const uint16_t* __restrict__ vh = a.v + head_off;
 
+  // ---- this lane's query, as the B operand of S^T = K Q^T
   const int qi = qb * BQ + wid * 32 + qn;
   bf16x8 qf[KS];
   {
@@ -104,6 +117,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     }
   }
 
+  // ---- the row's list
   int nblk, T;
   const int32_t* lidx = nullptr;
   const float* lw = nullptr;
@@ -117,8 +131,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     lidx = a.kv_idx + (size_t)row * a.cap;
     lw = a.inv_pi + (size_t)row * a.cap;
   }
-  if (T == 0) {
-    // empty list: the estimate is 0
+  if (T == 0) {  // empty list: the estimate is 0
     if (qi < a.L) {
 #pragma unroll
       for (int c = 0; c < D; c += 4) {
@@ -133,23 +146,40 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     return;
   }
 
-  // ---- list entries.  A wave-wide direct load covers KPI (<= BK) consecutive
-  // key rows, which lie in one block, so the entry it needs is wave-uniform.
-  // It is fetched with a vector load (a scalar load would share the LDS wait
-  // counter and, returning out of order, stall every LDS wait behind it) and
-  // made uniform when used.  Set F is fetched for tile n+3 during iteration n,
-  // used for K of n+3 in iteration n+1 and for V of n+3 in n+2.
-  static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
+  // ---- direct loads.  Buffer resources cover this head's K and V; a lane's
+  // offset is a per-lane constant (row within the block, swizzled chunk) plus
+  // the block's wave-uniform offset.  Keys past L read out of range (zero).
+  const uint32_t head_bytes = (uint32_t)a.L * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), 0, (int)head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), 0, (int)head_bytes, 0x00020000);
+  constexpr uint32_t OOB = 0x7FFFFFF0u;
+  uint32_t klane[NCH], vlane[NCH];
+  int rlane[NCH];  // row of this lane's load within its block
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ii = j * NW + wid;
+    const int kk = ii * KPI + lane / CPR, cp = lane % CPR;
+    const int ck = (D == 128) ? (cp ^ (kk & 15)) : (cp ^ ((kk >> 1) & 7));
+    const int cv = (D == 128) ? (cp ^ ((kk & 3) << 2)) : (cp ^ (((kk >> 1) & 1) << 2));
+    rlane[j] = kk % BK;
+    klane[j] = (uint32_t)(rlane[j] * D * 2 + ck * 16);
+    vlane[j] = (uint32_t)(rlane[j] * D * 2 + cv * 16);
+  }
+  // List entries: a wave-wide load covers KPI (<= BK) rows of one block, so
+  // its entry is wave-uniform.  Fetched with vector loads (scalar loads would
+  // share the LDS wait counter) three tiles ahead, made uniform when used.
   struct Entries {
-    int blk[NCH];  // wave-uniform block index of each wave-wide load
-    int bblk;      // threads 0..63: block of key `tid`
-    float bw;      //               and its weight
+    int blk[NCH];
+    int bblk;   // threads 0..63: block of key `tid`
+    float bw;   //               and its weight
   };
   auto fetch = [&](Entries& E, int tile) {
     if constexpr (!DENSE) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int kk = (j * NW + (tid >> 6)) * KPI + lane / CPR;  // same block for the whole wave
+        const int kk = (j * NW + (tid >> 6)) * KPI + lane / CPR;
         const int e = tile * SPT + kk / BK;
         const int ec = e < nblk ? e : nblk - 1;
         E.blk[j] = lidx[ec];
@@ -162,26 +192,23 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       }
     }
   };
-  // wave-wide direct loads of one tile of K or V (SWZ: 0 = K layout, 1 = V layout)
-  auto dma = [&](const uint16_t* __restrict__ src, unsigned char* buf, const Entries& E, int tile,
-                 auto SWZ) {
+  auto uniformize = [&](Entries& E) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) E.blk[j] = __builtin_amdgcn_readfirstlane(E.blk[j]);
+  };
+  auto dma = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&lanec)[NCH], unsigned char* buf,
+                 const Entries& E, int tile) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ii = j * NW + wid;                 // wave-wide load index: LDS positions [64 ii, 64 ii + 64)
-      const int kk = ii * KPI + lane / CPR;        // key row of this lane's position
-      const int cp = lane % CPR;                   // chunk position within the row
-      int c;
-      if constexpr (decltype(SWZ)::value == 0) c = (D == 128) ? (cp ^ (kk & 15)) : (cp ^ ((kk >> 1) & 7));
-      else c = (D == 128) ? (cp ^ ((kk & 7) << 1)) : (cp ^ ((kk & 3) << 1));
+      const int ii = j * NW + wid;
       const int e = tile * SPT + (ii * KPI) / BK;
       int blk;
       if constexpr (DENSE) blk = e;
-      else blk = e < nblk ? __builtin_amdgcn_readfirstlane(E.blk[j]) : -1;
-      const bool blk_ok = DENSE ? true : (blk >= 0 && blk < a.NK);
-      const int key = blk * BK + kk % BK;
-      const bool ok = blk_ok && key < a.L;
-      const uint16_t* g = src + (size_t)(ok ? key : 0) * D + c * 8;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(buf + ii * 1024), 16, 0, 0);
+      else blk = e < nblk ? E.blk[j] : -1;
+      const bool ok = DENSE ? true : (blk >= 0 && blk < a.NK);
+      uint32_t off = ok ? lanec[j] + (uint32_t)blk * (BK * D * 2) : OOB;
+      if (ok && blk * BK + BK > a.L && blk * BK + rlane[j] >= a.L) off = OOB;  // keys past L
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + ii * 1024), 16, off, 0, 0, 0);
     }
   };
   auto put_bias = [&](int slot, const Entries& E, int tile) {
@@ -195,9 +222,13 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       if (lane == 0) tail_s[slot] = any_tail != 0ull;
     }
   };
+  auto wait_dma_and_sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
+    __syncthreads();
+  };
 
-  // V^T transposing-read offsets (see v_off)
-  int voff[DB];
+  // ---- per-lane LDS read offsets
+  int voff[DB];  // V^T transposing reads (see v_off): 16-lane group G, lane s in it
   {
     const int G = lane >> 4, s = lane & 15;
     const int r0 = 4 * h + (s >> 2);
@@ -207,9 +238,6 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       voff[db] = v_off<D>(r0, col >> 3) + (col & 7) * 2;
     }
   }
-  int koff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = k_off<D>(qn, 2 * ks + h);  // rows qn and 32 + qn share it
 
   f32x16 acc[DB];
 #pragma unroll
@@ -224,19 +252,19 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
 
   auto qk = [&](const unsigned char* kb, f32x16 (&sacc)[2]) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + sb * 32 * (D * 2) + koff[ks]);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + k_off<D>(sb * 32 + qn, 2 * ks + h));
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], sacc[sb], 0, 0, 0);
       }
-    }
   };
-  // Logits of one tile: t = S scale log2(e) + log2(w) - m, with the bias read
-  // once per 4-key group (a group always lies in one block).  Returns this
-  // lane's max.  Branch-free, so it schedules together with the next tile's QK.
+  // t = S scale log2(e) + log2(w) - m, bias read once per 4-key group (a group
+  // always lies in one block); returns this lane's max
   auto logits = [&](f32x16 (&sacc)[2], int slot, float m_use) {
     float mt = -INFINITY;
 #pragma unroll
@@ -253,8 +281,8 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       }
     return mt;
   };
-  // Tiles holding keys past L inside a listed block (at most one per row):
-  // mask those keys individually and recompute the max.
+  // tiles with keys past L inside a listed block (at most one per row): mask
+  // those keys individually and recompute the max
   auto mask_tail = [&](f32x16 (&sacc)[2], int slot) {
     float mt = -INFINITY;
 #pragma unroll
@@ -267,8 +295,9 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       }
     return mt;
   };
-  // Rest of the softmax: move the reference if needed, P = 2^t in bf16, row sum.
-  auto finish_softmax = [&](f32x16 (&sacc)[2], float mt, float m_use, bf16x8 (&pf)[4]) {
+  // move the reference when a tile exceeds it by more than TAU (or on the first
+  // valid tile); afterwards sacc holds t relative to m_run
+  auto rescale = [&](f32x16 (&sacc)[2], float mt, float m_use) {
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     if (mt > TAU || (m_run == -INFINITY && mt > -INFINITY)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-mt);
@@ -283,6 +312,10 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[sb][r] -= mt;
     }
+  };
+  // P = 2^t rounded to bf16 in the PV operand layout; returns the row sum of
+  // exactly these rounded values
+  auto probs = [&](f32x16 (&sacc)[2], bf16x8 (&pf)[4]) {
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -297,7 +330,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
           pf[sb * 2 + half][e] = pk[0];
           pf[sb * 2 + half][e + 1] = pk[1];
         }
-    l_run += psum;
+    return psum;
   };
   auto pv = [&](const unsigned char* vb, const bf16x8 (&pf)[4]) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -314,58 +347,81 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       }
     }
   };
-  auto wait_dma_and_sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
-    __syncthreads();
-  };
 
-  // ---- schedule: slot p = n % 2 holds K, V and bias of tile n; the direct
-  // loads of tile n+1 into slot p^1 are issued before the compute of tile n
-  // and waited for at its end, followed by one barrier.
-  auto uniformize = [&](Entries& E) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) E.blk[j] = __builtin_amdgcn_readfirstlane(E.blk[j]);
-  };
-  Entries EC, EF;  // EC: entries of the tile whose loads are issued next; EF: being fetched
-  fetch(EC, 0);
-  if (T > 1) fetch(EF, 1);
-  uniformize(EC);
-  dma(kh, k_s0, EC, 0, std::integral_constant<int, 0>{});
-  dma(vh, v_s0, EC, 0, std::integral_constant<int, 1>{});
-  put_bias(0, EC, 0);
-  wait_dma_and_sync();
-  EC = EF;
-  uniformize(EC);
-  auto iteration = [&](int n, auto PAR) {
-    constexpr int p = decltype(PAR)::value;
-    unsigned char* k_cur = p ? k_s1 : k_s0;
-    unsigned char* v_cur = p ? v_s1 : v_s0;
-    unsigned char* k_nxt = p ? k_s0 : k_s1;
-    unsigned char* v_nxt = p ? v_s0 : v_s1;
-    if (n + 2 < T) fetch(EF, n + 2);
-    if (n + 1 < T) {
-      dma(kh, k_nxt, EC, n + 1, std::integral_constant<int, 0>{});
-      dma(vh, v_nxt, EC, n + 1, std::integral_constant<int, 1>{});
-      put_bias(p ^ 1, EC, n + 1);
+  // ---- prologue: zeroed slots, then K(0), bias(0), V(0), K(1), bias(1);
+  // S(0) = QK(0) and its logits
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < TILE; o += NT * 16) {
+      *reinterpret_cast<u32x4*>(k_s0 + o) = z;
+      *reinterpret_cast<u32x4*>(k_s1 + o) = z;
+      *reinterpret_cast<u32x4*>(v_s0 + o) = z;
+      *reinterpret_cast<u32x4*>(v_s1 + o) = z;
     }
-    f32x16 sacc[2];
-    qk(k_cur, sacc);
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float mt = logits(sacc, p, m_use);
-    if (tail_s[p]) mt = mask_tail(sacc, p);
+  }
+  Entries E0, E1, EK, EF;
+  fetch(E0, 0);
+  if (T > 1) fetch(E1, 1);
+  if (T > 2) fetch(EK, 2);
+  __syncthreads();  // the zeroing is done before any direct load lands
+  uniformize(E0);
+  dma(krs, klane, k_s0, E0, 0);
+  dma(vrs, vlane, v_s0, E0, 0);
+  put_bias(0, E0, 0);
+  if (T > 1) {
+    uniformize(E1);
+    dma(krs, klane, k_s1, E1, 1);
+    put_bias(1, E1, 1);
+  }
+  wait_dma_and_sync();
+  f32x16 sA[2], sB[2];
+  qk(k_s0, sA);
+  {
+    const float m_use = 0.f;
+    float mt = logits(sA, 0, m_use);
+    if (tail_s[0]) mt = mask_tail(sA, 0);
+    rescale(sA, mt, m_use);
+  }
+  __syncthreads();  // every wave is done with k_s0 before K(2) overwrites it
+  Entries EV = E1;  // entries of the next V load (tile n+1)
+  uniformize(EK);   // entries of the next K/bias load (tile n+2)
+
+  auto iteration = [&](int n, auto PAR, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int p = decltype(PAR)::value;
+    unsigned char* k_new = p ? k_s1 : k_s0;   // gets K(n+2)
+    unsigned char* k_nxt = p ? k_s0 : k_s1;   // holds K(n+1)
+    unsigned char* v_cur = p ? v_s1 : v_s0;   // holds V(n)
+    unsigned char* v_new = p ? v_s0 : v_s1;   // gets V(n+1)
+    if (n + 3 < T) fetch(EF, n + 3);
+    if (n + 2 < T) {
+      dma(krs, klane, k_new, EK, n + 2);
+      put_bias(p, EK, n + 2);
+    }
+    if (n + 1 < T) dma(vrs, vlane, v_new, EV, n + 1);
+    // phase A: QK(n+1) || probabilities of tile n
+    qk(k_nxt, s_nxt);
     bf16x8 pf[4];
-    finish_softmax(sacc, mt, m_use, pf);
+    l_run += probs(s_cur, pf);
+    // phase B: PV(n) || logits of tile n+1
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     pv(v_cur, pf);
+    float mt = logits(s_nxt, p ^ 1, m_use);
+    if (n + 1 < T) {
+      if (tail_s[p ^ 1]) mt = mask_tail(s_nxt, p ^ 1);
+      rescale(s_nxt, mt, m_use);
+    }
     wait_dma_and_sync();
-    EC = EF;
-    uniformize(EC);
+    EV = EK;
+    EK = EF;
+    uniformize(EK);
   };
 #pragma unroll 1
   for (int n = 0; n < T; n += 2) {
-    iteration(n, std::integral_constant<int, 0>{});
-    if (n + 1 < T) iteration(n + 1, std::integral_constant<int, 1>{});
+    iteration(n, std::integral_constant<int, 0>{}, sA, sB);
+    if (n + 1 < T) iteration(n + 1, std::integral_constant<int, 1>{}, sB, sA);
   }
 
+  // ---- epilogue: O = O^T / l, valid queries only
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qi < a.L) {
