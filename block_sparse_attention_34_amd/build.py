@@ -21,6 +21,8 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU forms stay off: plain fp32 code is what the kernels rely on
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a kernel whose host-side launch stub went missing fails here, not at load time
+    "-Wl,--no-undefined",
 ]
 
 

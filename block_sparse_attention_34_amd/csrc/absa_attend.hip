@@ -50,6 +50,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a first-class vector, kept in VGPRs
 
+// Lanes l and l + 32 hold the same query (different keys): v_permlane32_swap
+// exchanges the two halves of a register, giving each lane its partner's value.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // K, V and the per-key bias have separate two-slot LDS rings; K and the bias
 // run one tile ahead of V.  Iteration n overlaps the two matrix products with
 // the vector work of the neighbouring tile:
@@ -146,9 +157,11 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     return;
   }
 
-  // ---- direct loads.  Buffer resources cover this head's K and V; a lane's
-  // offset is a per-lane constant (row within the block, swizzled chunk) plus
-  // the block's wave-uniform offset.  Keys past L read out of range (zero).
+  // ---- direct loads.  Buffer resources cover this head's K and V (L*D*2
+  // bytes); a lane's offset is a per-lane constant (row within the block,
+  // swizzled chunk) plus the block's wave-uniform base.  Rows past L lie past
+  // the end of the resource and entries outside the list get a base past it:
+  // such loads land zeros.
   const uint32_t head_bytes = (uint32_t)a.L * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), 0, (int)head_bytes, 0x00020000);
@@ -156,69 +169,70 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), 0, (int)head_bytes, 0x00020000);
   constexpr uint32_t OOB = 0x7FFFFFF0u;
   uint32_t klane[NCH], vlane[NCH];
-  int rlane[NCH];  // row of this lane's load within its block
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int ii = j * NW + wid;
     const int kk = ii * KPI + lane / CPR, cp = lane % CPR;
     const int ck = (D == 128) ? (cp ^ (kk & 15)) : (cp ^ ((kk >> 1) & 7));
     const int cv = (D == 128) ? (cp ^ ((kk & 3) << 2)) : (cp ^ (((kk >> 1) & 1) << 2));
-    rlane[j] = kk % BK;
-    klane[j] = (uint32_t)(rlane[j] * D * 2 + ck * 16);
-    vlane[j] = (uint32_t)(rlane[j] * D * 2 + cv * 16);
+    klane[j] = (uint32_t)((kk % BK) * D * 2 + ck * 16);
+    vlane[j] = (uint32_t)((kk % BK) * D * 2 + cv * 16);
   }
-  // List entries: a wave-wide load covers KPI (<= BK) rows of one block, so
-  // its entry is wave-uniform.  Fetched with vector loads (scalar loads would
-  // share the LDS wait counter) three tiles ahead, made uniform when used.
+  // List entries.  A wave-wide load covers KPI (<= BK) rows of one block, so
+  // its entry is wave-uniform.  They are fetched one iteration ahead with
+  // vector loads (scalar loads would share the LDS wait counter), always
+  // (indices clamped to the list) so the destination registers are reused in
+  // place, and consumed after the barrier that ends the iteration.
   struct Entries {
     int blk[NCH];
-    int bblk;   // threads 0..63: block of key `tid`
-    float bw;   //               and its weight
+    int bblk;   // lane i: block of key i of the tile
+    float bw;   //         and its weight
   };
   auto fetch = [&](Entries& E, int tile) {
     if constexpr (!DENSE) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int kk = (j * NW + (tid >> 6)) * KPI + lane / CPR;
-        const int e = tile * SPT + kk / BK;
-        const int ec = e < nblk ? e : nblk - 1;
-        E.blk[j] = lidx[ec];
+        const int e = tile * SPT + ((j * NW + wid) * KPI) / BK;
+        E.blk[j] = lidx[e < nblk ? e : nblk - 1];
       }
-      if (tid < 64) {
-        const int e = tile * SPT + tid / BK;
-        const int ec = e < nblk ? e : nblk - 1;
-        E.bblk = lidx[ec];
-        E.bw = lw[ec];
+      const int e = tile * SPT + lane / BK;
+      const int ec = e < nblk ? e : nblk - 1;
+      E.bblk = lidx[ec];
+      E.bw = lw[ec];
+    }
+  };
+  // wave-uniform byte base of each wave-wide load of `tile`
+  auto bases = [&](const Entries& E, int tile, uint32_t (&base)[NCH]) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int e = tile * SPT + ((j * NW + wid) * KPI) / BK;
+      if constexpr (DENSE) {
+        base[j] = (uint32_t)e * (BK * D * 2);
+      } else {
+        const int blk = __builtin_amdgcn_readfirstlane(E.blk[j]);
+        const bool ok = e < nblk && blk >= 0 && blk < a.NK;
+        base[j] = ok ? (uint32_t)blk * (BK * D * 2) : OOB;
       }
     }
   };
-  auto uniformize = [&](Entries& E) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) E.blk[j] = __builtin_amdgcn_readfirstlane(E.blk[j]);
-  };
-  auto dma = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&lanec)[NCH], unsigned char* buf,
-                 const Entries& E, int tile) {
+  auto dma = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&lanec)[NCH], const uint32_t (&base)[NCH],
+                 unsigned char* buf) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ii = j * NW + wid;
-      const int e = tile * SPT + (ii * KPI) / BK;
-      int blk;
-      if constexpr (DENSE) blk = e;
-      else blk = e < nblk ? E.blk[j] : -1;
-      const bool ok = DENSE ? true : (blk >= 0 && blk < a.NK);
-      uint32_t off = ok ? lanec[j] + (uint32_t)blk * (BK * D * 2) : OOB;
-      if (ok && blk * BK + BK > a.L && blk * BK + rlane[j] >= a.L) off = OOB;  // keys past L
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + ii * 1024), 16, off, 0, 0, 0);
+      // (a named offset: an arithmetic expression in this argument position
+      // makes clang's host pass drop the kernel's launch stub)
+      const int off = (int)(lanec[j] + base[j]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + (j * NW + wid) * 1024), 16, off, 0, 0, 0);
     }
   };
   auto put_bias = [&](int slot, const Entries& E, int tile) {
     if (tid < 64) {
       const int e = tile * SPT + tid / BK;
-      const int blk = DENSE ? e : (e < nblk ? E.bblk : -1);
+      const int blk = DENSE ? e : E.bblk;
+      const bool ok = DENSE ? true : (e < nblk && blk >= 0 && blk < a.NK);
       const int key = blk * BK + tid % BK;
-      const bool slot_ok = DENSE ? true : (blk >= 0 && blk < a.NK);
-      bias_s[slot][tid] = (slot_ok && key < a.L) ? (DENSE ? 0.f : __log2f(E.bw)) : -INFINITY;
-      const unsigned long long any_tail = __ballot(slot_ok && key >= a.L);
+      bias_s[slot][tid] = (ok && key < a.L) ? (DENSE ? 0.f : __log2f(E.bw)) : -INFINITY;
+      const unsigned long long any_tail = __ballot(ok && key >= a.L);
       if (lane == 0) tail_s[slot] = any_tail != 0ull;
     }
   };
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   // move the reference when a tile exceeds it by more than TAU (or on the first
   // valid tile); afterwards sacc holds t relative to m_run
   auto rescale = [&](f32x16 (&sacc)[2], float mt, float m_use) {
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = half_swap_max(mt);
     if (mt > TAU || (m_run == -INFINITY && mt > -INFINITY)) {
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-mt);
       l_run *= alpha;
@@ -359,18 +373,22 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       *reinterpret_cast<u32x4*>(v_s1 + o) = z;
     }
   }
-  Entries E0, E1, EK, EF;
+  Entries E0, E1, EN;
   fetch(E0, 0);
-  if (T > 1) fetch(E1, 1);
-  if (T > 2) fetch(EK, 2);
+  fetch(E1, 1);
+  fetch(EN, 2);
   __syncthreads();  // the zeroing is done before any direct load lands
-  uniformize(E0);
-  dma(krs, klane, k_s0, E0, 0);
-  dma(vrs, vlane, v_s0, E0, 0);
-  put_bias(0, E0, 0);
+  uint32_t vb[NCH];  // bases of the next V load
+  {
+    uint32_t b0[NCH];
+    bases(E0, 0, b0);
+    dma(krs, klane, b0, k_s0);
+    dma(vrs, vlane, b0, v_s0);
+    put_bias(0, E0, 0);
+  }
   if (T > 1) {
-    uniformize(E1);
-    dma(krs, klane, k_s1, E1, 1);
+    bases(E1, 1, vb);
+    dma(krs, klane, vb, k_s1);
     put_bias(1, E1, 1);
   }
   wait_dma_and_sync();
@@ -383,21 +401,22 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     rescale(sA, mt, m_use);
   }
   __syncthreads();  // every wave is done with k_s0 before K(2) overwrites it
-  Entries EV = E1;  // entries of the next V load (tile n+1)
-  uniformize(EK);   // entries of the next K/bias load (tile n+2)
 
+  // EN holds the entries of tile n+2 (landed); vb the bases of V(n+1)
   auto iteration = [&](int n, auto PAR, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     constexpr int p = decltype(PAR)::value;
     unsigned char* k_new = p ? k_s1 : k_s0;   // gets K(n+2)
     unsigned char* k_nxt = p ? k_s0 : k_s1;   // holds K(n+1)
     unsigned char* v_cur = p ? v_s1 : v_s0;   // holds V(n)
     unsigned char* v_new = p ? v_s0 : v_s1;   // gets V(n+1)
-    if (n + 3 < T) fetch(EF, n + 3);
+    uint32_t bn[NCH];
     if (n + 2 < T) {
-      dma(krs, klane, k_new, EK, n + 2);
-      put_bias(p, EK, n + 2);
+      bases(EN, n + 2, bn);
+      dma(krs, klane, bn, k_new);
+      put_bias(p, EN, n + 2);
     }
-    if (n + 1 < T) dma(vrs, vlane, v_new, EV, n + 1);
+    fetch(EN, n + 3);
+    if (n + 1 < T) dma(vrs, vlane, vb, v_new);
     // phase A: QK(n+1) || probabilities of tile n
     qk(k_nxt, s_nxt);
     bf16x8 pf[4];
@@ -411,9 +430,8 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
       rescale(s_nxt, mt, m_use);
     }
     wait_dma_and_sync();
-    EV = EK;
-    EK = EF;
-    uniformize(EK);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) vb[j] = bn[j];
   };
 #pragma unroll 1
   for (int n = 0; n < T; n += 2) {
@@ -422,7 +440,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   }
 
   // ---- epilogue: O = O^T / l, valid queries only
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qi < a.L) {
     const size_t obase = head_off + (size_t)qi * D;
