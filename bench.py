@@ -40,17 +40,23 @@ def parse():
     return ap.parse_args()
 
 
+def attend_source_digest():
+    """First 16 hex digits of the sha256 over the gather-attention kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("absa_attend_tiles.h", "absa_attend.hip", "absa_attend_pp.hip"):
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_34_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload_tag="wan14b_720p"):
     """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if
     it was taken on the current kernel source (else None: the kernel changed since)."""
-    import hashlib
     prof = os.path.join(ROOT, "profiles", f"attend_kernel_{workload_tag}_traffic.md")
-    src = os.path.join(ROOT, "block_sparse_attention_34_amd", "csrc", "absa_attend.hip")
     try:
         fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line
                       and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "attend_source_sha256_16"))
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if fields.get("attend_source_sha256_16") == cur:
+        if fields.get("attend_source_sha256_16") == attend_source_digest():
             return int(fields["traffic_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         pass

@@ -21,45 +21,11 @@
 // tile n+1 load while tile n computes (two LDS slots, one barrier per tile).
 #include <type_traits>
 
+#include "absa_attend_tiles.h"
 #include "absa_device.h"
 #include "absa_launch.h"
 
 namespace absa {
-
-// LDS tiles hold 64 keys x D bf16 row-major, 16-byte chunks xor-swizzled by row.
-// K tile: chunk c of row kk at c ^ (kk & 15) (D = 128) so that the 16 rows read
-// by a quarter-wave (one 16-byte chunk each) hit distinct bank groups.
-template <int D>
-__device__ __forceinline__ int k_off(int kk, int c) {
-  if constexpr (D == 128) return kk * 256 + ((c ^ (kk & 15)) << 4);
-  else return kk * 128 + ((c ^ ((kk >> 1) & 7)) << 4);
-}
-
-// V tile: chunk c of row kk at c ^ 4 (kk & 3) (D = 128; D = 64: c ^ 4 ((kk >> 1) & 1)).
-// V is read with ds_read_b64_tr_b16: a half-wave reads 4 consecutive rows x 64
-// bytes (chunks 4 db .. 4 db + 3); the xor moves each row's four chunks to a
-// different quarter of the banks (for D = 64, rows of equal parity share a bank
-// half and the xor separates them).
-template <int D>
-__device__ __forceinline__ int v_off(int kk, int c) {
-  if constexpr (D == 128) return kk * 256 + ((c ^ ((kk & 3) << 2)) << 4);
-  else return kk * 128 + ((c ^ (((kk >> 1) & 1) << 2)) << 4);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a first-class vector, kept in VGPRs
-
-// Lanes l and l + 32 hold the same query (different keys): v_permlane32_swap
-// exchanges the two halves of a register, giving each lane its partner's value.
-__device__ __forceinline__ float half_swap_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // K, V and the per-key bias have separate two-slot LDS rings; K and the bias
 // run one tile ahead of V.  Iteration n overlaps the two matrix products with
@@ -71,7 +37,6 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // l of a wave writes LDS base + 16 l); the row swizzle is applied by choosing
 // which chunk each lane fetches.  The loop is unrolled by two so every ring
 // slot is a distinct static LDS array.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Two workgroups of 256 threads per CU (at most 256 VGPRs per lane) hide the
 // barrier of one behind the matrix work of the other.
@@ -173,8 +138,7 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
   for (int j = 0; j < NCH; ++j) {
     const int ii = j * NW + wid;
     const int kk = ii * KPI + lane / CPR, cp = lane % CPR;
-    const int ck = (D == 128) ? (cp ^ (kk & 15)) : (cp ^ ((kk >> 1) & 7));
-    const int cv = (D == 128) ? (cp ^ ((kk & 3) << 2)) : (cp ^ (((kk >> 1) & 1) << 2));
+    const int ck = k_chunk<D>(kk, cp), cv = v_chunk<D>(kk, cp);
     klane[j] = (uint32_t)((kk % BK) * D * 2 + ck * 16);
     vlane[j] = (uint32_t)((kk % BK) * D * 2 + cv * 16);
   }
@@ -347,7 +311,6 @@ __global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLa
     return psum;
   };
   auto pv = [&](const unsigned char* vb, const bf16x8 (&pf)[4]) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -487,11 +450,10 @@ static hipError_t launch_bk(const AttendLaunch& a, hipStream_t st, bool dense) {
   }
 }
 
+// 128-query blocks run on the two-row kernel (absa_attend_pp.hip)
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense) {
-  if (a.d == 128) {
-    return a.Bq == 128 ? launch_bk<128, 128>(a, st, dense) : launch_bk<128, 64>(a, st, dense);
-  }
-  return a.Bq == 128 ? launch_bk<64, 128>(a, st, dense) : launch_bk<64, 64>(a, st, dense);
+  if (a.Bq == 128) return launch_attend_pp(a, st, dense);
+  return a.d == 128 ? launch_bk<128, 64>(a, st, dense) : launch_bk<64, 64>(a, st, dense);
 }
 
 }  // namespace absa

@@ -1,0 +1,506 @@
+// Gather-attention for 128-query blocks on gfx950, two rows per workgroup in
+// anti-phase (AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği",
+// third item: KV blocks much smaller than a tile are packed into full
+// matrix-core tiles; SIP item: the 1/pi weights act inside the softmax
+// numerator and denominator).  Dense attention is the same pipeline with
+// contiguous KV tiles and unit weights.
+//
+// The arithmetic per tile is that of the one-row kernel (absa_attend.hip):
+// S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with the queries
+// in the N position, so every lane owns one query and the softmax statistics
+// stay in-lane.  What differs is the schedule.  A tile's work splits into a
+// matrix phase (QK of the next tile and PV of the current one: 32 MFMAs and all
+// LDS reads) and a vector phase (logits, running max, 2^t, bf16 rounding, row
+// sums, and the direct loads of later tiles).  On a SIMD the matrix core and the
+// vector ALU only overlap when the two streams come from different waves, so a
+// workgroup holds two rows (8 waves, one wave of each row per SIMD) and runs
+// them half a period apart: while row A's waves are in their matrix phase, row
+// B's waves are in their vector phase, and the roles swap at every barrier.
+//
+// Before the phase loop each row loads tiles 0 and 1 and computes QK(0).  Then,
+// per row, local phase j (row B runs one global step behind row A):
+//   j = 2m        vector phase of tile m: softmax -> P(m); loads of K(m+2),
+//                 V(m+1), bias(m+2) and the list entries of tile m+3
+//   j = 2m + 1    matrix phase: QK(m+1) and PV(m)
+// K and V have two LDS slots each, the bias four.  A load issued in the vector
+// phase of tile m is first read two global steps later; each barrier waits only
+// for the loads of earlier phases, so they stay in flight across one barrier.
+#include <type_traits>
+
+#include "absa_attend_tiles.h"
+#include "absa_device.h"
+#include "absa_launch.h"
+
+namespace absa {
+
+template <int D, int BK, bool DENSE, bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
+  constexpr int BQ = 128;
+  constexpr int HT = 256;              // threads per row
+  constexpr int NW = 4;                // waves per row, 32 queries each
+  constexpr int CPR = D / 8;           // 16-byte chunks per key row
+  constexpr int KPI = 64 / CPR;        // key rows covered by one wave-wide 16-byte load
+  constexpr int NCH = 64 * CPR / HT;   // wave-wide loads per thread per tile and tensor
+  constexpr int SPT = 64 / BK;         // list entries per 64-key tile
+  constexpr int KS = D / 16;           // k-steps of the QK product
+  constexpr int DB = D / 32;           // 32-wide d blocks of O
+  constexpr int TILE = 64 * D * 2;
+  constexpr float TAU = 8.f;           // the running max moves only when exceeded by this
+  static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
+
+  struct alignas(16) RowLds {
+    unsigned char k[2][TILE];
+    unsigned char v[2][TILE];
+  };
+  __shared__ RowLds sh[2];
+
+  // Pairs of rows.  Workgroups are dealt round-robin over the 8 XCDs; within a
+  // run of 8*32 workgroups, XCD x takes the 32 adjacent pairs [32x, 32x+32), i.e.
+  // 64 adjacent query blocks of one head, whose lists overlap in that XCD's L2.
+  const int npairs = (a.rows + 1) >> 1;
+  int pair = blockIdx.x;
+  {
+    constexpr int R = 32, S = 8 * R;
+    const int g = pair / S, i = pair % S;
+    if ((g + 1) * S <= npairs) pair = g * S + (i & 7) * R + (i >> 3);
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wid >> 2, wq = wid & 3;
+  const int h = lane >> 5, qn = lane & 31;
+  RowLds& R = sh[half];
+
+  auto list_len = [&](int r, int& nb) {
+    if constexpr (DENSE) {
+      nb = (a.L + BK - 1) / BK;
+      return (a.L + 63) / 64;
+    } else {
+      int c = a.count[r];
+      c = c < 0 ? 0 : (c > a.cap ? a.cap : c);
+      nb = c;
+      return (c + SPT - 1) / SPT;
+    }
+  };
+  const int row = 2 * pair + half, orow = 2 * pair + (1 - half);
+  int nblk = 0, onb = 0;
+  const int T = row < a.rows ? list_len(row, nblk) : 0;
+  const int To = orow < a.rows ? list_len(orow, onb) : 0;
+  const int rowc = row < a.rows ? row : a.rows - 1;  // a valid row for address arithmetic
+  const int bh = rowc / a.NQ, qb = rowc % a.NQ;
+  const size_t head_off = (size_t)bh * a.L * D;
+  const int qi = qb * BQ + wq * 32 + qn;
+  const bool qvalid = row < a.rows && qi < a.L;
+
+  if (row < a.rows && T == 0 && qvalid) {  // empty list: the estimate is 0
+#pragma unroll
+    for (int c = 0; c < D; c += 4) {
+      if constexpr (OUT_BF16)
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o) + head_off + (size_t)qi * D + c) =
+            make_uint2(0, 0);
+      else
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + head_off + (size_t)qi * D + c) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // ---- this lane's query, as the B operand of S^T = K Q^T
+  bf16x8 qf[KS];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + head_off + (size_t)(qvalid ? qi : 0) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = qp[2 * ks + h];
+      if (!qvalid) w = u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int32_t* lidx = DENSE ? nullptr : a.kv_idx + (size_t)rowc * a.cap;
+  const float* lw = DENSE ? nullptr : a.inv_pi + (size_t)rowc * a.cap;
+
+  // ---- direct loads (as in the one-row kernel): buffer resources cover this
+  // head's K and V (L*D*2 bytes); rows past L lie past the end of the resource
+  // and entries outside the list get a base past it, so such loads land zeros.
+  const uint32_t head_bytes = (uint32_t)a.L * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), 0, (int)head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), 0, (int)head_bytes, 0x00020000);
+  constexpr uint32_t OOB = 0x7FFFFFF0u;
+  uint32_t klane[NCH], vlane[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int kk = (j * NW + wq) * KPI + lane / CPR, cp = lane % CPR;
+    klane[j] = (uint32_t)((kk % BK) * D * 2 + k_chunk<D>(kk, cp) * 16);
+    vlane[j] = (uint32_t)((kk % BK) * D * 2 + v_chunk<D>(kk, cp) * 16);
+  }
+  // List entries, decoded lane-parallel: for a tile, lane i handles entry
+  // tile*SPT + (i % SPT).  They are fetched one vector phase ahead with vector
+  // loads, always (indices clamped to the list), so the destination registers
+  // are reused in place.
+  struct Entry {
+    int blk;
+    float w;
+  };
+  auto fetch = [&](Entry& E, int tile) {
+    if constexpr (!DENSE) {
+      const int last = nblk > 0 ? nblk - 1 : 0;
+      const int e = tile * SPT + lane % SPT;
+      const int ec = e < last ? e : last;
+      E.blk = lidx[ec];
+      E.w = lw[ec];
+    }
+  };
+  // A decoded tile: the wave-uniform byte base of each wave-wide load, the
+  // bias log2(w) of each entry (lane i holds entry i; -inf for entries outside
+  // the list), and the mask of its keys that lie past L (a listed block that
+  // holds key L-1).
+  struct Tile {
+    float bias;
+    unsigned long long past;
+  };
+  auto decode = [&](const Entry& E, int tile, uint32_t (&base)[NCH], Tile& t) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) base[j] = (uint32_t)tile * (BK * D * 2);  // past the end: zeros
+      t.bias = tile * 64 < a.L ? 0.f : -INFINITY;
+      t.past = __ballot(tile * 64 < a.L && tile * 64 + lane >= a.L);
+    } else {
+      const int e = tile * SPT + lane % SPT;
+      const bool ok = e < nblk && (unsigned)E.blk < (unsigned)a.NK;
+      const uint32_t bb = ok ? (uint32_t)E.blk * (BK * D * 2) : OOB;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) base[j] = __builtin_amdgcn_readlane(bb, ((j * NW + wq) * KPI) / BK);
+      t.bias = ok ? __log2f(E.w) : -INFINITY;
+      t.past = 0ull;
+      if (__ballot(ok && (E.blk + 1) * BK > a.L) != 0ull) {  // the block holding key L-1 (rare)
+        // key k of the tile lies in entry k / BK, row k % BK
+        int kb = 0;
+        bool kok = false;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+          const int bi = __builtin_amdgcn_readlane(E.blk, i);
+          const bool oki = __builtin_amdgcn_readlane((int)ok, i) != 0;
+          if (lane / BK == i) {
+            kb = bi;
+            kok = oki;
+          }
+        }
+        t.past = __ballot(kok && kb * BK + lane % BK >= a.L);
+      }
+    }
+  };
+  auto dma = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&lanec)[NCH], const uint32_t (&base)[NCH],
+                 unsigned char* buf) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      // (a named offset: an arithmetic expression in this argument position
+      // makes clang's host pass drop the kernel's launch stub)
+      const int off = (int)(lanec[j] + base[j]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + (j * NW + wq) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets
+  int koff[KS];  // K rows qn (and qn + 32 at +32 rows), chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = k_off<D>(qn, 2 * ks + h);
+  int voff[DB];  // V^T transposing reads: 16-lane group G, lane s in it
+  {
+    const int G = lane >> 4, s = lane & 15;
+    const int r0 = 4 * h + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (s & 3);
+      voff[db] = v_off<D>(r0, col >> 3) + (col & 7) * 2;
+    }
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 sacc[2];
+  u32x4 pf[4];  // P of the current tile, bf16 pairs in the PV operand layout
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};  // row 1's first PV uses P = 0
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+  bf16x2 ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
+
+  // ---- matrix work
+  auto qk = [&](const unsigned char* kb) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 kfrag = *reinterpret_cast<const bf16x8*>(kb + koff[ks] + sb * 32 * (D * 2));
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], sacc[sb], 0, 0, 0);
+      }
+  };
+  auto pv = [&](const unsigned char* vb) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const unsigned char* p0 = vb + voff[db] + (16 * ks) * (D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * (D * 2)));
+        const i16x4 w[2] = {lo, hi};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
+                                                          __builtin_bit_cast(bf16x8, pf[ks]), acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- vector work.  t = S scale log2(e) + log2(w) - m; a 4-key group of a
+  // lane always lies in one entry, the same one for every lane; returns this
+  // lane's max
+  auto logits = [&](const Tile& tl, float m_use) {
+    float cb[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+      cb[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tl.bias), i)) - m_use;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float cg = cb[(32 * sb + 8 * g4) / BK];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float tv = fmaf(sacc[sb][4 * g4 + i], sl2, cg);
+          sacc[sb][4 * g4 + i] = tv;
+          mt = fmaxf(mt, tv);
+        }
+      }
+    return mt;
+  };
+  // a tile with keys past L: mask them individually and recompute the max
+  // (element r of half sb holds key 32 sb + 8 (r / 4) + 4 h + r % 4)
+  auto mask_tail = [&](const Tile& tl) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const uint32_t w = (uint32_t)(tl.past >> (32 * sb)) >> (4 * h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if ((w >> (8 * (r >> 2) + (r & 3))) & 1u) sacc[sb][r] = -INFINITY;
+        mt = fmaxf(mt, sacc[sb][r]);
+      }
+    }
+    return mt;
+  };
+  // move the reference when a tile exceeds it by more than TAU (or on the first
+  // valid tile); afterwards sacc holds t relative to m_run
+  // (The branch is taken by the whole wave when any lane needs it, lanes that
+  // do not rescale by 1: a lane-divergent branch around the O^T accumulators
+  // makes the compiler keep a second copy of them.)
+  auto rescale = [&](float mt, float m_use) {
+    mt = half_swap_max(mt);
+    const bool need = mt > TAU || (m_run == -INFINITY && mt > -INFINITY);
+    if (__ballot(need) != 0ull) {
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(-mt)) : 1.f;
+      const float shift = need ? mt : 0.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_run = need ? m_use + mt : m_run;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] -= shift;
+    }
+  };
+  // P = 2^t rounded to bf16 in the PV operand layout; returns the row sum of
+  // exactly these rounded values
+  // (packed bf16 pairs: P lives across a barrier, and as a vector of single
+  // bf16 elements it would occupy twice the registers)
+  auto probs = [&]() {
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16x2 pk;
+          pk[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e]);
+          pk[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e + 1]);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, psum, false);
+          w[e] = __builtin_bit_cast(uint32_t, pk);
+        }
+        pf[sb * 2 + hf] = w;
+      }
+    return psum;
+  };
+
+  // ---- the two rows' phase sequences on one barrier.  Iteration it: row 0
+  // runs vector(it) then matrix(it); row 1 runs matrix(it - 1) then vector(it).
+  // Both rows run the same number of iterations: phases of tiles past a row's
+  // list are neutral (their K and V slots hold zeros, their bias is -inf, so P
+  // is 0 and neither O, nor the running max, nor the row sum changes), which
+  // keeps the loop free of branches around the accumulators.
+  Entry EN;           // list entries of tile m+2 (fetched in the previous vector phase)
+  uint32_t vb[NCH];   // bases of the next V load
+  Tile tc, tn;        // decoded tiles m and m+1
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};  // V slot 1 is read (times P = 0) before its first load
+    for (int o = (tid & 255) * 16; o < TILE; o += HT * 16) *reinterpret_cast<u32x4*>(R.v[1] + o) = z;
+    Entry E0, E1;
+    fetch(E0, 0);
+    fetch(E1, 1);
+    fetch(EN, 2);
+    uint32_t b0[NCH];
+    decode(E0, 0, b0, tc);
+    dma(krs, klane, b0, R.k[0]);
+    dma(vrs, vlane, b0, R.v[0]);
+    decode(E1, 1, vb, tn);
+    dma(krs, klane, vb, R.k[1]);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+
+  // The direct loads follow the vector work they would otherwise delay: the
+  // four vector-phase waves of a CU share one address unit, and a wave's
+  // in-order issue stalls behind a queue of loads.
+  auto vector_phase = [&](int m) {
+    const int p = m & 1;
+    uint32_t kn[NCH];
+    Tile t2;
+    decode(EN, m + 2, kn, t2);
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float mt = logits(tc, m_use);
+    dma(krs, klane, kn, R.k[p]);  // K(m+2)
+    if (tc.past != 0ull) mt = mask_tail(tc);
+    rescale(mt, m_use);
+    l_run += probs();
+    dma(vrs, vlane, vb, R.v[p ^ 1]);  // V(m+1)
+    fetch(EN, m + 3);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) vb[q] = kn[q];
+    tc = tn;
+    tn = t2;
+    // the loads of earlier phases have landed (this phase issued at least
+    // 2*NCH direct loads after them, and loads return in order); this
+    // phase's may stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((2 * NCH) | 0x0070);  // vmcnt(2 NCH) lgkmcnt(0)
+  };
+  // QK(m+1) (for m = -1: QK(0); past the list: zeros) and PV(m)
+  auto matrix_phase = [&](int m) {
+    const int p = m & 1;
+    qk(R.k[p ^ 1]);
+    pv(R.v[p]);
+    // LDS reads run ahead of the matrix products that consume them: RA up
+    // front, then one (K) or two (V) after every product
+    constexpr int RA = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - RA / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 2 * KS - RA / 2; i < 2 * KS + 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  };
+  // barrier without a memory fence (each phase ends with its own waits); no
+  // instruction may be scheduled across it, so the phases stay apart
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Each row runs its own loop (straight-line bodies keep the accumulators in
+  // place); both execute 2*NIT barriers, which the hardware counts per
+  // workgroup wherever they sit in the code.
+  const int T0 = half == 0 ? T : To, T1 = half == 0 ? To : T;
+  const int NIT = T0 > T1 + 1 ? T0 : T1 + 1;
+  if (half == 0) {
+    qk(R.k[0]);
+#pragma unroll 1
+    for (int it = 0; it < NIT; ++it) {
+      vector_phase(it);
+      barrier();
+      matrix_phase(it);
+      barrier();
+    }
+  } else {
+#pragma unroll 1
+    for (int it = 0; it < NIT; ++it) {
+      matrix_phase(it - 1);
+      barrier();
+      vector_phase(it);
+      barrier();
+    }
+  }
+
+  // ---- epilogue: O = O^T / l, valid queries only
+  if (T > 0) {
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qvalid) {
+      const size_t obase = head_off + (size_t)qi * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dc = db * 32 + 8 * g4 + 4 * h;
+          const float o0 = acc[db][4 * g4 + 0] * inv, o1 = acc[db][4 * g4 + 1] * inv;
+          const float o2 = acc[db][4 * g4 + 2] * inv, o3 = acc[db][4 * g4 + 3] * inv;
+          if constexpr (OUT_BF16) {
+            const __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1, b2 = (__bf16)o2, b3 = (__bf16)o3;
+            const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+            const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o) + obase + dc) = make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + obase + dc) = make_float4(o0, o1, o2, o3);
+          }
+        }
+    }
+  }
+}
+
+template <int D, int BK, bool DENSE>
+static hipError_t launch_pp_t(const AttendLaunch& a, hipStream_t st) {
+  dim3 grid((a.rows + 1) / 2);
+  if (a.out_bf16)
+    attend_pp_kernel<D, BK, DENSE, true><<<grid, 512, 0, st>>>(a);
+  else
+    attend_pp_kernel<D, BK, DENSE, false><<<grid, 512, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_pp_bk(const AttendLaunch& a, hipStream_t st, bool dense) {
+  if (dense) return launch_pp_t<D, 64, true>(a, st);
+  switch (a.Bk) {
+    case 16: return launch_pp_t<D, 16, false>(a, st);
+    case 32: return launch_pp_t<D, 32, false>(a, st);
+    default: return launch_pp_t<D, 64, false>(a, st);
+  }
+}
+
+hipError_t launch_attend_pp(const AttendLaunch& a, hipStream_t st, bool dense) {
+  return a.d == 128 ? launch_pp_bk<128>(a, st, dense) : launch_pp_bk<64>(a, st, dense);
+}
+
+}  // namespace absa

@@ -51,5 +51,6 @@ inline int logit_splits(int NQ, int C, int BH, int NKp, int* tiles_per_split) {
 hipError_t launch_select(const SelectLaunch& a, hipStream_t st);
 hipError_t configure_select_kernels();
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense);
+hipError_t launch_attend_pp(const AttendLaunch& a, hipStream_t st, bool dense);
 
 }  // namespace absa
