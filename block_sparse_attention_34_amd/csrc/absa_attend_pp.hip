@@ -222,8 +222,6 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   f32x16 sacc[2];
   u32x4 pf[4];  // P of the current tile, bf16 pairs in the PV operand layout
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};  // row 1's first PV uses P = 0
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
   bf16x2 ones;
@@ -344,9 +342,9 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     return psum;
   };
 
-  // ---- the two rows' phase sequences on one barrier.  Iteration it: row 0
-  // runs vector(it) then matrix(it); row 1 runs matrix(it - 1) then vector(it).
-  // Both rows run the same number of iterations: phases of tiles past a row's
+  // ---- the two rows' phase sequences on one barrier: row 0 runs vector(0),
+  // matrix(0), vector(1), ... while row 1 runs the same sequence one step
+  // later.  Both rows run the same number of iterations: phases of tiles past a row's
   // list are neutral (their K and V slots hold zeros, their bias is -inf, so P
   // is 0 and neither O, nor the running max, nor the row sum changes), which
   // keeps the loop free of branches around the accumulators.
@@ -354,8 +352,6 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   uint32_t vb[NCH];   // bases of the next V load
   Tile tc, tn;        // decoded tiles m and m+1
   {
-    const u32x4 z = {0u, 0u, 0u, 0u};  // V slot 1 is read (times P = 0) before its first load
-    for (int o = (tid & 255) * 16; o < TILE; o += HT * 16) *reinterpret_cast<u32x4*>(R.v[1] + o) = z;
     Entry E0, E1;
     fetch(E0, 0);
     fetch(E1, 1);
@@ -396,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((2 * NCH) | 0x0070);  // vmcnt(2 NCH) lgkmcnt(0)
   };
-  // QK(m+1) (for m = -1: QK(0); past the list: zeros) and PV(m)
+  // QK(m+1) (past the list: zeros) and PV(m)
   auto matrix_phase = [&](int m) {
     const int p = m & 1;
     qk(R.k[p ^ 1]);
@@ -427,29 +423,21 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Each row runs its own loop (straight-line bodies keep the accumulators in
-  // place); both execute 2*NIT barriers, which the hardware counts per
-  // workgroup wherever they sit in the code.
-  const int T0 = half == 0 ? T : To, T1 = half == 0 ? To : T;
-  const int NIT = T0 > T1 + 1 ? T0 : T1 + 1;
-  if (half == 0) {
-    qk(R.k[0]);
+  // Both rows run the same loop body; row 1 passes one barrier before it and
+  // row 0 one after it, which puts row 1 one step behind (both execute
+  // 2*NIT + 1 barriers, which the hardware counts per workgroup wherever they
+  // sit in the code).
+  const int NIT = T > To ? T : To;
+  qk(R.k[0]);
+  if (half == 1) barrier();
 #pragma unroll 1
-    for (int it = 0; it < NIT; ++it) {
-      vector_phase(it);
-      barrier();
-      matrix_phase(it);
-      barrier();
-    }
-  } else {
-#pragma unroll 1
-    for (int it = 0; it < NIT; ++it) {
-      matrix_phase(it - 1);
-      barrier();
-      vector_phase(it);
-      barrier();
-    }
+  for (int it = 0; it < NIT; ++it) {
+    vector_phase(it);
+    barrier();
+    matrix_phase(it);
+    barrier();
   }
+  if (half == 0) barrier();
 
   // ---- epilogue: O = O^T / l, valid queries only
   if (T > 0) {
