@@ -36,8 +36,110 @@ def parse():
     ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1920)
-    ap.add_argument("--extra", action="store_true", help="also time dense and top-k ablations")
+    ap.add_argument("--extra", action="store_true", help="also time the dense kernel")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the JSON line: accuracy and time of SIP / top-k / block-size / prior-art "
+                         "selection against dense attention, as a markdown table")
     return ap.parse_args()
+
+
+def ablation(args):
+    """Error of the estimator against dense attention (rel-L2 over the whole output) and the time of
+    selection and attention, for: SIP at three budgets and three seeds, top-k truncation at the same
+    budgets, the KV block size at a 10% budget, and the coarse prior-art arm (one mean query per block,
+    top-k, 64-key blocks).  On three inputs: the workload as generated (its 10x-norm outlier tokens act
+    as attention sinks: about one effective key per query), and the same recipe without outlier tokens
+    with queries scaled by 1/4 and by 1/8 (more diffuse attention); the effective number of keys per
+    query (exp of the softmax entropy, mean over sampled rows) is printed for each.
+    Times are HIP-event means over 5 launches after 2 warm-ups."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_34_amd as absa
+    from workloads import gen_config
+
+    from workloads import CONFIGS, gen_fourier_heads
+
+    wl = gen_config(3, kv_block=16)
+    dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)  # noqa: E731
+    stream = torch.cuda.current_stream()
+    dense_flops = 4.0 * wl.B * wl.H * float(wl.L) ** 2 * wl.d
+
+    def timed(fn, n=5):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    p16 = absa.Problem(wl.B, wl.H, wl.L, wl.d, wl.T, wl.Hs, wl.Ws, wl.q_block, 16)
+    o_dense = torch.empty((p16.B, p16.H, p16.L, p16.d), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(o_dense)
+    sample = np.random.default_rng(12345).choice(p16.rows, 16, replace=False)
+    print(f"Workload: {wl.name} (B={wl.B}, H={wl.H}, L={wl.L}, d={wl.d}, Bq={wl.q_block}).\n")
+    spec = CONFIGS[3]
+    for outliers, temp in ((True, 1.0), (False, 0.25), (False, 0.125)):
+        # same recipe and seed, with or without the outlier tokens
+        qn, kn, vn = gen_fourier_heads(spec.T, spec.Hs, spec.Ws, spec.d, spec.modes, spec.noise_std, outliers,
+                                       3, list(range(spec.H)))
+        sh = (1, spec.H, spec.L, spec.d)
+        q0, k, v = dev(qn.reshape(sh)), dev(kn.reshape(sh)), dev(vn.reshape(sh))
+        del qn, kn, vn
+        q = (q0.float() * temp).to(torch.bfloat16).contiguous()
+        t_dense = timed(lambda: absa.dense(p16, q, k, v, out=o_dense))
+        ref_norm = float(torch.linalg.vector_norm(o_dense))
+        eff = []
+        for r in sample:
+            bh, qb = divmod(int(r), p16.nq)
+            qs = q[0, bh, qb * wl.q_block: min((qb + 1) * wl.q_block, wl.L)].float()
+            pr = torch.softmax(qs @ k[0, bh].float().T / math.sqrt(wl.d), dim=1)
+            eff.append(float(torch.exp(-(pr * torch.log(pr + 1e-30)).sum(1)).mean()))
+        rows = []
+
+        def run(label, Bk, keep, mode, seed, clusters=4):
+            p = absa.Problem(wl.B, wl.H, wl.L, wl.d, wl.T, wl.Hs, wl.Ws, wl.q_block, Bk)
+            lists = absa.alloc_lists(p)
+            ws = torch.empty(absa.select_workspace_bytes(p, keep, clusters=clusters, mode=mode),
+                             dtype=torch.uint8, device="cuda")
+            sel = lambda: absa.select(p, q, k, keep, clusters=clusters, seed=seed, mode=mode,  # noqa: E731
+                                      lists=lists, workspace=ws)
+            t_sel = timed(sel)
+            t_att = timed(lambda: absa.attend(p, q, k, v, lists, out=o))
+            err = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
+            kept = float(lists.count.double().mean()) / p.nk
+            rows.append((label, Bk, keep, seed, clusters, kept, err, t_sel, t_att))
+            print(f"[ablation] temp {temp} {label} Bk={Bk} keep={keep} seed={seed} C={clusters}: "
+                  f"rel-L2 {err:.4e} select {t_sel:.2f} ms attend {t_att:.2f} ms", file=sys.stderr, flush=True)
+
+        for keep in (0.08, 0.095, 0.11):
+            for seed in (0, 1, 2):
+                run("IBCS+SIP", 16, keep, "sip", seed)
+            run("IBCS+top-k", 16, keep, "topk", 0)
+        for Bk in (16, 32, 64):
+            run("IBCS+SIP", Bk, 0.10, "sip", 0)
+            run("IBCS+top-k", Bk, 0.10, "topk", 0)
+        run("mean query+top-k (prior art)", 64, 0.10, "topk", 0, clusters=1)
+        run("mean query+SIP", 64, 0.10, "sip", 0, clusters=1)
+
+        print(f"### {'with' if outliers else 'without'} outlier tokens, queries scaled by {temp}: effective keys per query "
+              f"{np.mean(eff):.1f}; dense attention {t_dense:.2f} ms "
+              f"({dense_flops / (t_dense * 1e-3) / 1e12:.0f} TFLOP/s)\n")
+        print("| selection | Bk | keep | seed | C | kept fraction | rel-L2 vs dense | select ms | attend ms |"
+              " dense-equiv. TFLOP/s (select+attend) |")
+        print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+        for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
+            print(f"| {label} | {Bk} | {keep:.3f} | {seed} | {C} | {kept:.4f} | {err:.3e} | {ts:.2f} | {ta:.2f} | "
+                  f"{dense_flops / ((ts + ta) * 1e-3) / 1e12:.0f} |")
+        sip = {}
+        for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
+            if label == "IBCS+SIP" and Bk == 16 and keep in (0.08, 0.095, 0.11):
+                sip.setdefault(keep, []).append(err)
+        print("\nSIP rel-L2, mean +- sd over seeds 0-2 (Bk 16): " + "; ".join(
+            f"keep {kp:.3f}: {np.mean(e):.3e} +- {np.std(e, ddof=1):.1e}" for kp, e in sip.items()) + "\n", flush=True)
 
 
 def attend_source_digest():
@@ -103,6 +205,9 @@ def cpu_baseline(wl, keep, kv_block, nrows):
 
 def main():
     args = parse()
+    if args.gpus == 1 and args.ablation:
+        ablation(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (heads shard "
               f"across GPUs with no communication; run one process per GPU).", file=sys.stderr)
