@@ -348,51 +348,65 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // list are neutral (their K and V slots hold zeros, their bias is -inf, so P
   // is 0 and neither O, nor the running max, nor the row sum changes), which
   // keeps the loop free of branches around the accumulators.
-  Entry EN;           // list entries of tile m+2 (fetched in the previous vector phase)
-  uint32_t vb[NCH];   // bases of the next V load
-  Tile tc, tn;        // decoded tiles m and m+1
+  // Per-row pipeline state entering vector(m): sacc holds the logits of tile m
+  // (relative to the reference in force when they were formed) and mt their
+  // per-lane maximum; t1, t2 are the decoded tiles m+1, m+2 (vector(m) decodes
+  // tile m+3 into t3); kn the K bases of tile m+2, vb the V bases of tile m+1;
+  // EN the list entries of tile m+3.
+  Entry EN;
+  uint32_t kn[NCH], vb[NCH];
+  Tile t1, t2, t3;
+  float mt;
+  auto form_logits = [&](const Tile& tl) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float x = logits(tl, m_use);
+    if (tl.past != 0ull) x = mask_tail(tl);
+    return x;
+  };
   {
-    Entry E0, E1;
+    Entry E0, E1, E2;
     fetch(E0, 0);
     fetch(E1, 1);
-    fetch(EN, 2);
+    fetch(E2, 2);
+    fetch(EN, 3);
     uint32_t b0[NCH];
-    decode(E0, 0, b0, tc);
+    Tile t0;
+    decode(E0, 0, b0, t0);
     dma(krs, klane, b0, R.k[0]);
     dma(vrs, vlane, b0, R.v[0]);
-    decode(E1, 1, vb, tn);
+    decode(E1, 1, vb, t1);
     dma(krs, klane, vb, R.k[1]);
+    decode(E2, 2, kn, t2);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    qk(R.k[0]);
+    mt = form_logits(t0);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  __syncthreads();
 
-  // The direct loads follow the vector work they would otherwise delay: the
-  // four vector-phase waves of a CU share one address unit, and a wave's
-  // in-order issue stalls behind a queue of loads.
+  // vector(m): softmax of tile m -> P(m); then the direct loads of K(m+2) and
+  // V(m+1), after the vector work they would otherwise delay (the four
+  // vector-phase waves of a CU share one address unit, and a wave's in-order
+  // issue stalls behind a queue of loads); then the decoding of tile m+3's
+  // entries and the fetch of tile m+4's
   auto vector_phase = [&](int m) {
     const int p = m & 1;
-    uint32_t kn[NCH];
-    Tile t2;
-    decode(EN, m + 2, kn, t2);
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float mt = logits(tc, m_use);
-    dma(krs, klane, kn, R.k[p]);  // K(m+2)
-    if (tc.past != 0ull) mt = mask_tail(tc);
     rescale(mt, m_use);
     l_run += probs();
+    dma(krs, klane, kn, R.k[p]);      // K(m+2)
     dma(vrs, vlane, vb, R.v[p ^ 1]);  // V(m+1)
-    fetch(EN, m + 3);
 #pragma unroll
     for (int q = 0; q < NCH; ++q) vb[q] = kn[q];
-    tc = tn;
-    tn = t2;
-    // the loads of earlier phases have landed (this phase issued at least
-    // 2*NCH direct loads after them, and loads return in order); this
-    // phase's may stay in flight
+    decode(EN, m + 3, kn, t3);
+    fetch(EN, m + 4);
+    // the loads of earlier phases have landed (this phase issued 2*NCH direct
+    // loads after them, and loads return in order); this phase's may stay in
+    // flight
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((2 * NCH) | 0x0070);  // vmcnt(2 NCH) lgkmcnt(0)
   };
-  // QK(m+1) (past the list: zeros) and PV(m)
+  // matrix(m): QK(m+1) (past the list: zeros) and PV(m); then the logits of
+  // tile m+1, which balances the two phases
   auto matrix_phase = [&](int m) {
     const int p = m & 1;
     qk(R.k[p ^ 1]);
@@ -411,6 +425,9 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    mt = form_logits(t1);
+    t1 = t2;
+    t2 = t3;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   };
@@ -428,7 +445,6 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // 2*NIT + 1 barriers, which the hardware counts per workgroup wherever they
   // sit in the code).
   const int NIT = T > To ? T : To;
-  qk(R.k[0]);
   if (half == 1) barrier();
 #pragma unroll 1
   for (int it = 0; it < NIT; ++it) {
