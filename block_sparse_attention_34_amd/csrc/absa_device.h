@@ -109,6 +109,62 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
   return t;
 }
 
+// Wave totals through DPP: pairwise within quads, then rotations within each
+// 16-lane row, then the four row sums read in lane order.  Every lane returns
+// the same value, and it does not depend on lane timing (only lanes 0, 16, 32
+// and 48 are read after the rotations).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x128>(v);  // row_ror:8
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ int wave_total_i(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  v += __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true);
+  v += __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Block totals of a float and an int together, one barrier: `redf`/`redi` hold
+// two buffers of NT/64 entries used alternately (`parity`), so a buffer is only
+// rewritten after every thread has passed the barrier that follows its last read.
+template <int NT>
+__device__ __forceinline__ void block_total2(float& fv, int& iv, float* redf, int* redi, int parity) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  fv = wave_total(fv);
+  iv = wave_total_i(iv);
+  float* rf = redf + parity * (NT / 64);
+  int* ri = redi + parity * (NT / 64);
+  if (lane == 0) {
+    rf[wid] = fv;
+    ri[wid] = iv;
+  }
+  __syncthreads();
+  float t = 0.f;
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    t += rf[w];
+    c += ri[w];
+  }
+  fv = t;
+  iv = c;
+}
+
 // Exclusive prefix sum in thread order and the total.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {

@@ -369,6 +369,60 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
 // Bernoulli draws (or top-k / all), and compaction into the row's list.
 constexpr int SIP_NT = 256;
 
+// Capping rounds of the SIP inclusion probabilities over one thread's chunk of
+// n <= PM block scores s[b0 .. b0+n).  The chunk stays in registers; each round
+// caps the free blocks with s R >= S_U and, in the same block reduction, forms
+// the sum over the blocks still free, which is the next round's S_U (the same
+// set, summed in the same order, as a fresh sum over the free blocks).  On
+// return flag[] holds 1 for capped, 0 for free (s > 0), 2 for zero blocks, and
+// R, S_U the remaining budget and free-score sum of the last round.
+template <int PM>
+__device__ __forceinline__ void sip_capping(const float* s, int b0, int n, float& R, float& S_U, unsigned char* flag,
+                                            float* redf, int* redi) {
+  float sv[PM];
+  uint64_t freem = 0ull, capm = 0ull;
+  float part = 0.f;
+  int nfree = 0;
+#pragma unroll
+  for (int e = 0; e < PM; ++e) {
+    sv[e] = (e < n) ? s[b0 + e] : 0.f;
+    if (sv[e] > 0.f) {
+      freem |= 1ull << e;
+      part += sv[e];
+      ++nfree;
+    }
+  }
+  int parity = 0;
+  block_total2<SIP_NT>(part, nfree, redf, redi, parity);
+  S_U = part;
+#pragma unroll 1
+  while (nfree > 0) {
+    int ncap = 0;
+    part = 0.f;
+#pragma unroll
+    for (int e = 0; e < PM; ++e) {
+      if ((freem >> e) & 1ull) {
+        if (__fmul_rn(sv[e], R) >= S_U) {
+          freem &= ~(1ull << e);
+          capm |= 1ull << e;
+          ++ncap;
+        } else {
+          part += sv[e];
+        }
+      }
+    }
+    parity ^= 1;
+    block_total2<SIP_NT>(part, ncap, redf, redi, parity);
+    if (ncap == 0) break;
+    S_U = part;
+    R -= (float)ncap;
+    nfree -= ncap;
+  }
+#pragma unroll
+  for (int e = 0; e < PM; ++e)
+    if (e < n) flag[b0 + e] = ((capm >> e) & 1ull) ? 1 : (sv[e] > 0.f ? 0 : 2);
+}
+
 template <int C>
 __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ logit,
                                                      const float2* __restrict__ mz, int nsplit,
@@ -383,8 +437,8 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
                                                      float* __restrict__ pi_out) {
   extern __shared__ float s[];                      // [NK]
   unsigned char* flag = reinterpret_cast<unsigned char*>(s + NK);  // [NK]
-  __shared__ float redf[SIP_NT / 64];
-  __shared__ int redi[SIP_NT / 64];
+  __shared__ float redf[2 * (SIP_NT / 64)];
+  __shared__ int redi[2 * (SIP_NT / 64)];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const int bh = row / NQ, i = row % NQ;
@@ -453,24 +507,11 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
     if (nstar >= (float)NK) {
       for (int b = b0; b < b1; ++b) flag[b] = 1;
     } else {
-      for (int b = b0; b < b1; ++b) flag[b] = (s[b] > 0.f) ? 0 : 2;
-      int nfree = 0;
-      for (int b = b0; b < b1; ++b) nfree += (flag[b] == 0);
-      nfree = block_sum_i<SIP_NT>(nfree, redi);
-#pragma unroll 1
-      while (nfree > 0) {
-        float part = 0.f;
-        for (int b = b0; b < b1; ++b)
-          if (flag[b] == 0) part += s[b];
-        S_U = block_sum<SIP_NT>(part, redf);
-        int ncap = 0;
-        for (int b = b0; b < b1; ++b)
-          if (flag[b] == 0 && __fmul_rn(s[b], R) >= S_U) { flag[b] = 1; ++ncap; }
-        ncap = block_sum_i<SIP_NT>(ncap, redi);
-        if (ncap == 0) break;
-        R -= (float)ncap;
-        nfree -= ncap;
-      }
+      const int n = b1 - b0;
+      if (P <= 16) sip_capping<16>(s, b0, n, R, S_U, flag, redf, redi);
+      else if (P <= 24) sip_capping<24>(s, b0, n, R, S_U, flag, redf, redi);
+      else if (P <= 32) sip_capping<32>(s, b0, n, R, S_U, flag, redf, redi);
+      else sip_capping<48>(s, b0, n, R, S_U, flag, redf, redi);
     }
   } else if (mode == 1) {
     // top-k*: largest bit pattern T with #{s >= T} >= k*, then the lowest-index ties
