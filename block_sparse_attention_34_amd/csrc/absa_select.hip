@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
                                                          float alpha) {
   constexpr int KS = D / 2;  // k-steps of 2 dims
   __shared__ __attribute__((aligned(16))) float kt[2][D * 32];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) index
   const int h = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int m0 = blockIdx.x * 128 + w * 32;
@@ -310,7 +311,14 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
   };
   fetch(tile0);
   put(0);
-  float* out_base = logit + (size_t)bh * M * NK;
+  // this wave's output window: logit rows m0 .. m0+31 (those below M) of the head
+  const int rows_here = max(0, min(32, M - m0));
+  const uint64_t obase = (uint64_t)(logit + ((size_t)bh * M + (rows_here > 0 ? m0 : 0)) * NK);
+  const uint32_t obase_lo = __builtin_amdgcn_readfirstlane((uint32_t)obase);
+  const uint32_t obase_hi = __builtin_amdgcn_readfirstlane((uint32_t)(obase >> 32));
+  const int obytes = __builtin_amdgcn_readfirstlane(rows_here * NK * 4);
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(((uint64_t)obase_hi << 32) | obase_lo), 0, obytes, 0x00020000);
   // running max m and normaliser Z = sum nk 2^(l - m) of the 16 centroids this
   // lane sees (terms more than 64 octaves below the max dropped)
   float rm[16], rz[16];
@@ -327,21 +335,25 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(areg[s2], kt[buf][(2 * s2 + h) * 32 + n], acc, 0, 0, 0);
+    // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
+    // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
+    // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z, and their
+    // stores (like those of rows >= M) fall outside the window and are dropped.
     const int b = tile * 32 + n;
-    if (b < NK) {
-      const float nk = (float)min(Bk, L - b * Bk);
+    const bool bv = b < NK;
+    const float nk = (float)min(Bk, L - b * Bk);
+    const int vo = bv ? (4 * h * NK + b) * 4 : 0x7FFFFFF0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float l = alpha * acc[r];
-        if (m < M) out_base[(size_t)m * NK + b] = l;
-        const float mn = fmaxf(rm[r], l);
-        const float d0 = rm[r] - mn, d1 = l - mn;
-        const float e0 = d0 >= -64.f ? exp2_split(d0) : 0.f;
-        const float e1 = d1 >= -64.f ? exp2_split(d1) : 0.f;
-        rz[r] = fmaf(rz[r], e0, nk * e1);
-        rm[r] = mn;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float l = bv ? alpha * acc[r] : -INFINITY;
+      const uint32_t lbits = __float_as_uint(l);
+      const int so = (8 * (r >> 2) + (r & 3)) * NK * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(lbits, ors, vo, so, 0);
+      const float dd = fabsf(rm[r] - l);
+      const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
+      const bool up = l > rm[r];
+      rz[r] = fmaf(rz[r], up ? e : 1.f, up ? nk : nk * e);
+      rm[r] = up ? l : rm[r];
     }
     if (tile + 1 < tile1) put(buf ^ 1);
   }
