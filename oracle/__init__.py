@@ -5,4 +5,8 @@ may import this package.  The HIP library never calls it and shares no code
 with it.
 """
 from .absa_oracle import *  # noqa: F401,F403
-from .absa_oracle import __all__  # noqa: F401
+from .absa_oracle import __all__ as _base_all
+from .fp8_oracle import *  # noqa: F401,F403
+from .fp8_oracle import __all__ as _fp8_all
+
+__all__ = list(_base_all) + list(_fp8_all)
