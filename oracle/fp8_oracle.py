@@ -19,14 +19,17 @@ F0  E4M3 is the OCP 8-bit format E4M3FN: bias 7, 3 mantissa bits, subnormals
     Encoding rounds to nearest, ties to the even code; a negative input that
     rounds to zero gives -0 (0x80).  The scales below keep every quantised
     input within +-448 (beyond that the encoder here saturates).
-F1  Q: one scale per token, s_Q = max_c |q_c| / 448 (fp32), codes e4m3(q / s_Q).
+    Every scale below is a power of two, s = 2^e with e the smallest integer
+    for which max |x| <= 448 s (s = 1 for an all-zero set), so dividing by it
+    is exact and only the E4M3 rounding loses information.
+F1  Q: one scale per token, s_Q from max_c |q_c|, codes e4m3(q / s_Q).
 F2  K: first centred by its per-head mean over all L tokens (a shift common to
     every key of a head leaves each query's softmax unchanged), k' = k - kbar
-    in fp32; then one scale per KV block, s_K = max |k'| / 448 over the
-    block's valid keys, codes e4m3(k' / s_K).
+    in fp32; then one scale per KV block, s_K from max |k'| over the block's
+    valid keys, codes e4m3(k' / s_K).
 F3  V: per KV block the mean of its valid keys, rounded to bf16 (mu_hat); the
     residual r = v - mu_hat (fp32) is quantised with one scale per channel and
-    head, s_V[c] = max_t |r[t][c]| / 448, codes e4m3(r / s_V).  The value
+    head, s_V[c] from max_t |r[t][c]|, codes e4m3(r / s_V).  The value
     reconstructed for key t of block b is mu_hat_b + s_V * dec(code).
 F4  Logits in log2 units: y = 8 (l - m) + 120 with l = sigma log2(e) s_Q s_K
     (q8 . k8) + log2 w_b, formed in fp32 by one fused multiply-add from the
@@ -56,7 +59,7 @@ import numpy as np
 from .absa_oracle import num_blocks, valid_len
 
 __all__ = [
-    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round",
+    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "pow2_scale",
     "quantize_q", "smooth_k", "quantize_k", "quantize_v", "Fp8Head",
     "quantize_head", "expcast_p", "attend_row_fp8", "attend_all_fp8",
 ]
@@ -117,10 +120,15 @@ def bf16_round(x) -> np.ndarray:
     return u.astype(np.uint32).view(_F32)
 
 
-def _scale(amax: np.ndarray) -> np.ndarray:
-    amax = np.asarray(amax, dtype=_F32)
-    s = amax / _F32(E4M3_MAX)
-    return np.where(amax > 0, s, _F32(1.0)).astype(_F32)
+def pow2_scale(amax) -> np.ndarray:
+    """2^e with e the smallest integer such that amax <= 448 * 2^e (1 where amax == 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)                        # amax = m 2^k, m in [0.5, 1); 448 = 0.875 2^9
+    e = np.where(m <= 0.875, k - 9, k - 8)
+    return np.where(amax > 0, np.ldexp(1.0, e), 1.0).astype(_F32)
+
+
+_scale = pow2_scale
 
 
 # ----------------------------------------------------------------------------- F1-F3
