@@ -48,11 +48,14 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   constexpr float TAU = 8.f;           // the running max moves only when exceeded by this
   static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
 
-  struct alignas(16) RowLds {
-    unsigned char k[2][TILE];
-    unsigned char v[2][TILE];
-  };
-  __shared__ RowLds sh[2];
+  // Each K/V slot is an LDS object of its own and the phase loop is unrolled
+  // by two, so every slot a phase touches is a compile-time constant: the
+  // compiler can then tell that a phase's LDS reads never alias the direct
+  // loads in flight into the other slots, and it adds no waits for them
+  // (with one shared object it waited for every direct load before the
+  // matrix phase's first V read).  [row][bytes]
+  __shared__ __attribute__((aligned(16))) unsigned char k_s0[2][TILE], k_s1[2][TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char v_s0[2][TILE], v_s1[2][TILE];
 
   // Pairs of rows.  Workgroups are dealt round-robin over the 8 XCDs; within a
   // run of 8*32 workgroups, XCD x takes the 32 adjacent pairs [32x, 32x+32), i.e.
@@ -68,7 +71,10 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = wid >> 2, wq = wid & 3;
   const int h = lane >> 5, qn = lane & 31;
-  RowLds& R = sh[half];
+  unsigned char* const K0 = k_s0[half];
+  unsigned char* const K1 = k_s1[half];
+  unsigned char* const V0 = v_s0[half];
+  unsigned char* const V1 = v_s1[half];
 
   auto list_len = [&](int r, int& nb) {
     if constexpr (DENSE) {
@@ -372,14 +378,14 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     uint32_t b0[NCH];
     Tile t0;
     decode(E0, 0, b0, t0);
-    dma(krs, klane, b0, R.k[0]);
-    dma(vrs, vlane, b0, R.v[0]);
+    dma(krs, klane, b0, K0);
+    dma(vrs, vlane, b0, V0);
     decode(E1, 1, vb, t1);
-    dma(krs, klane, vb, R.k[1]);
+    dma(krs, klane, vb, K1);
     decode(E2, 2, kn, t2);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    qk(R.k[0]);
+    qk(K0);
     mt = form_logits(t0);
   }
 
@@ -388,13 +394,14 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // vector-phase waves of a CU share one address unit, and a wave's in-order
   // issue stalls behind a queue of loads); then the decoding of tile m+3's
   // entries and the fetch of tile m+4's
-  auto vector_phase = [&](int m) {
-    const int p = m & 1;
+  // (pc: the parity of m as a compile-time constant, which names the slots)
+  auto vector_phase = [&](auto pc, int m) {
+    constexpr int p = decltype(pc)::value;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     rescale(mt, m_use);
     l_run += probs();
-    dma(krs, klane, kn, R.k[p]);      // K(m+2)
-    dma(vrs, vlane, vb, R.v[p ^ 1]);  // V(m+1)
+    dma(krs, klane, kn, p ? K1 : K0);  // K(m+2)
+    dma(vrs, vlane, vb, p ? V0 : V1);  // V(m+1)
 #pragma unroll
     for (int q = 0; q < NCH; ++q) vb[q] = kn[q];
     decode(EN, m + 3, kn, t3);
@@ -407,10 +414,10 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   };
   // matrix(m): QK(m+1) (past the list: zeros) and PV(m); then the logits of
   // tile m+1, which balances the two phases
-  auto matrix_phase = [&](int m) {
-    const int p = m & 1;
-    qk(R.k[p ^ 1]);
-    pv(R.v[p]);
+  auto matrix_phase = [&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    qk(p ? K0 : K1);
+    pv(p ? V1 : V0);
     // LDS reads run ahead of the matrix products that consume them: RA up
     // front, then one (K) or two (V) after every product
     constexpr int RA = 4;
@@ -446,12 +453,20 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // sit in the code).
   const int NIT = T > To ? T : To;
   if (half == 1) barrier();
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
 #pragma unroll 1
-  for (int it = 0; it < NIT; ++it) {
-    vector_phase(it);
+  for (int it = 0; it < NIT; it += 2) {
+    vector_phase(even, it);
     barrier();
-    matrix_phase(it);
+    matrix_phase(even);
     barrier();
+    if (it + 1 < NIT) {
+      vector_phase(odd, it + 1);
+      barrier();
+      matrix_phase(odd);
+      barrier();
+    }
   }
   if (half == 0) barrier();
 
