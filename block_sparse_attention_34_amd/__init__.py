@@ -16,6 +16,7 @@ from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
 __all__ = [
     "Problem", "BlockLists", "select", "attend", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
+    "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
 ]
 
 _MODES = {"sip": SEL_SIP, "topk": SEL_TOPK, "all": SEL_ALL}
@@ -177,4 +178,71 @@ def dense(prob: Problem, q, k, v, out=None):
     st = library().absa_dense(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               _stream())
     _lib.check(st, "absa_dense")
+    return out
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3) path
+
+class Fp8Operands(NamedTuple):
+    """Quantised operands (absa_fp8_operands): device tensors owned by the caller."""
+    q8: "object"    # uint8 [B,H,L,128]
+    sq: "object"    # float32 [B,H,L]
+    k8: "object"    # uint8 [B,H,L,128]
+    sk: "object"    # float32 [B,H,NK]
+    kbar: "object"  # float32 [B,H,128]
+    v8t: "object"   # uint8 [B,H,NK,128,16]
+    sv: "object"    # float32 [B,H,128]
+    mu: "object"    # int16 (bf16 bits) [B,H,NK,32,4]
+
+    def c(self) -> _lib.AbsaFp8Operands:
+        return _lib.AbsaFp8Operands(*(t.data_ptr() for t in self))
+
+
+def alloc_fp8(prob: Problem, device) -> Fp8Operands:
+    import torch
+    B, H, L, nk = prob.B, prob.H, prob.L, prob.nk
+    u8, f32 = torch.uint8, torch.float32
+    return Fp8Operands(
+        torch.empty((B, H, L, 128), dtype=u8, device=device), torch.empty((B, H, L), dtype=f32, device=device),
+        torch.empty((B, H, L, 128), dtype=u8, device=device), torch.empty((B, H, nk), dtype=f32, device=device),
+        torch.empty((B, H, 128), dtype=f32, device=device), torch.empty((B, H, nk, 128, 16), dtype=u8, device=device),
+        torch.empty((B, H, 128), dtype=f32, device=device), torch.empty((B, H, nk, 32, 4), dtype=torch.int16,
+                                                                        device=device))
+
+
+def fp8_workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t()
+    p = prob.c()
+    _lib.check(library().absa_fp8_workspace(ctypes.byref(p), ctypes.byref(n)), "absa_fp8_workspace")
+    return n.value
+
+
+def quantize_fp8(prob: Problem, q, k, v, ops: Optional[Fp8Operands] = None, workspace=None):
+    """E4M3 operands of bf16 Q, K, V (d = 128, Bk = 16).  Returns (ops, workspace)."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    ops = alloc_fp8(prob, q.device) if ops is None else ops
+    nbytes = fp8_workspace_bytes(prob)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    o = ops.c()
+    st = library().absa_quantize_fp8(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(o),
+                                     workspace.data_ptr(), workspace.numel(), _stream())
+    _lib.check(st, "absa_quantize_fp8")
+    return ops, workspace
+
+
+def attend_fp8(prob: Problem, ops: Fp8Operands, lists: Optional[BlockLists], out=None):
+    """FP8 block-sparse attention over ``lists`` (None: every key, weight 1).  Returns O."""
+    import torch
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=ops.q8.device)
+    p = prob.c()
+    o = ops.c()
+    bl = lists.c() if lists is not None else None
+    st = library().absa_attend_fp8(ctypes.byref(p), ctypes.byref(o), ctypes.byref(bl) if bl is not None else None,
+                                   out.data_ptr(), _stream())
+    _lib.check(st, "absa_attend_fp8")
     return out

@@ -18,6 +18,7 @@ SEL_SIP, SEL_TOPK, SEL_ALL = 0, 1, 2
 EXPORTED = (
     "absa_version", "absa_status_string", "absa_num_blocks", "absa_select_workspace",
     "absa_select_workspace_layout", "absa_select", "absa_attend", "absa_dense",
+    "absa_fp8_workspace", "absa_quantize_fp8", "absa_attend_fp8",
 )
 
 
@@ -42,6 +43,13 @@ class AbsaBlockList(ctypes.Structure):
     _fields_ = [
         ("count", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("inv_pi", ctypes.c_void_p),
         ("cap", ctypes.c_int32),
+    ]
+
+
+class AbsaFp8Operands(ctypes.Structure):
+    _fields_ = [
+        ("q8", ctypes.c_void_p), ("sq", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("sk", ctypes.c_void_p),
+        ("kbar", ctypes.c_void_p), ("v8t", ctypes.c_void_p), ("sv", ctypes.c_void_p), ("mu", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +89,13 @@ def load() -> ctypes.CDLL:
     lib.absa_attend.argtypes = [P, vp, vp, vp, BL, vp, vp]
     lib.absa_dense.restype = ctypes.c_int
     lib.absa_dense.argtypes = [P, vp, vp, vp, vp, vp]
+    F8 = ctypes.POINTER(AbsaFp8Operands)
+    lib.absa_fp8_workspace.restype = ctypes.c_int
+    lib.absa_fp8_workspace.argtypes = [P, ctypes.POINTER(sz)]
+    lib.absa_quantize_fp8.restype = ctypes.c_int
+    lib.absa_quantize_fp8.argtypes = [P, vp, vp, vp, F8, vp, sz, vp]
+    lib.absa_attend_fp8.restype = ctypes.c_int
+    lib.absa_attend_fp8.argtypes = [P, F8, BL, vp, vp]
     _lib = lib
     return lib
 

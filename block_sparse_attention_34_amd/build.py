@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["absa_api.hip", "absa_select.hip", "absa_attend.hip", "absa_attend_pp.hip"]
+SOURCES = ["absa_api.hip", "absa_select.hip", "absa_attend.hip", "absa_attend_pp.hip", "absa_fp8.hip"]
 LIB = os.path.join(PKG, "libabsa.so")
 
 HIPCC_FLAGS = [

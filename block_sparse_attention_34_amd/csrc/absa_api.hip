@@ -106,6 +106,44 @@ absa_status check_lists(const absa_blocklist* l, bool need_cap_nk, int NK) {
   return ABSA_OK;
 }
 
+// FP8 path: d = 128, Bk = 16 (and Bq = 128 for the attention step)
+absa_status check_fp8_problem(const absa_problem* p, Dims* dm, bool attend) {
+  absa_status st = check_problem(p, dm);
+  if (st != ABSA_OK) return st;
+  if (p->d != 128 || p->kv_block != 16) return ABSA_ERR_UNSUPPORTED;
+  if (attend && p->q_block != 128) return ABSA_ERR_UNSUPPORTED;
+  // byte offsets inside one head's operands are 32-bit
+  if ((int64_t)p->L * 128 > INT32_MAX / 2) return ABSA_ERR_UNSUPPORTED;
+  return ABSA_OK;
+}
+
+absa_status check_fp8_operands(const absa_fp8_operands* o) {
+  if (!o || !o->q8 || !o->sq || !o->k8 || !o->sk || !o->kbar || !o->v8t || !o->sv || !o->mu)
+    return ABSA_ERR_INVALID_ARG;
+  const void* ps[] = {o->q8, o->sq, o->k8, o->sk, o->kbar, o->v8t, o->sv, o->mu};
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return ABSA_ERR_ALIGNMENT;
+  return ABSA_OK;
+}
+
+struct Fp8Ws {
+  size_t ksum, vmax, mu_nat, total;
+};
+
+Fp8Ws fp8_ws(const Dims& dm) {
+  const size_t nchunk = (size_t)(dm.NK + 15) / 16;
+  Fp8Ws w;
+  size_t o = 0;
+  w.ksum = o;
+  o = align_up(o + (size_t)dm.BH * nchunk * 128 * sizeof(double), kWsAlign);
+  w.vmax = o;
+  o = align_up(o + (size_t)dm.BH * nchunk * 128 * sizeof(float), kWsAlign);
+  w.mu_nat = o;
+  o = align_up(o + (size_t)dm.BH * dm.NK * 128 * sizeof(uint16_t), kWsAlign);
+  w.total = o;
+  return w;
+}
+
 std::once_flag g_attr_once;
 hipError_t g_attr_err = hipSuccess;
 
@@ -270,6 +308,91 @@ absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, 
 absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
                        void* stream) {
   return attend_common(prob, q, k, v, nullptr, o, stream, true);
+}
+
+absa_status absa_fp8_workspace(const absa_problem* prob, size_t* bytes) {
+  if (!bytes) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  absa_status st = check_fp8_problem(prob, &dm, false);
+  if (st != ABSA_OK) return st;
+  *bytes = fp8_ws(dm).total;
+  return ABSA_OK;
+}
+
+absa_status absa_quantize_fp8(const absa_problem* prob, const void* q, const void* k, const void* v,
+                              const absa_fp8_operands* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Dims dm;
+  absa_status st = check_fp8_problem(prob, &dm, false);
+  if (st != ABSA_OK) return st;
+  if (!q || !k || !v) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ABSA_ERR_ALIGNMENT;
+  st = check_fp8_operands(out);
+  if (st != ABSA_OK) return st;
+  const Fp8Ws w = fp8_ws(dm);
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+  char* ws = static_cast<char*>(workspace);
+  absa::QuantFp8Launch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.BH = (int)dm.BH;
+  a.L = prob->L;
+  a.NK = dm.NK;
+  a.q8 = out->q8;
+  a.sq = out->sq;
+  a.k8 = out->k8;
+  a.sk = out->sk;
+  a.kbar = out->kbar;
+  a.v8t = out->v8t;
+  a.sv = out->sv;
+  a.mu = out->mu;
+  a.ksum_part = reinterpret_cast<double*>(ws + w.ksum);
+  a.vmax_part = reinterpret_cast<float*>(ws + w.vmax);
+  a.mu_nat = reinterpret_cast<uint16_t*>(ws + w.mu_nat);
+  hipError_t e = absa::launch_quantize_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
+absa_status absa_attend_fp8(const absa_problem* prob, const absa_fp8_operands* ops,
+                            const absa_blocklist* lists, void* o, void* stream) {
+  Dims dm;
+  absa_status st = check_fp8_problem(prob, &dm, true);
+  if (st != ABSA_OK) return st;
+  st = check_fp8_operands(ops);
+  if (st != ABSA_OK) return st;
+  if (!o) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
+  const bool dense = lists == nullptr;
+  if (!dense) {
+    st = check_lists(lists, false, dm.NK);
+    if (st != ABSA_OK) return st;
+  }
+  absa::AttendFp8Launch a{};
+  a.q8 = ops->q8;
+  a.sq = ops->sq;
+  a.k8 = ops->k8;
+  a.sk = ops->sk;
+  a.v8t = ops->v8t;
+  a.sv = ops->sv;
+  a.mu = ops->mu;
+  a.o = o;
+  a.L = prob->L;
+  a.NQ = dm.NQ;
+  a.NK = dm.NK;
+  a.rows = (int)dm.rows;
+  a.out_bf16 = prob->out_bf16;
+  const float scale = prob->scale > 0.f ? prob->scale : 1.0f / std::sqrt((float)prob->d);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (!dense) {
+    a.count = lists->count;
+    a.kv_idx = lists->kv_idx;
+    a.inv_pi = lists->inv_pi;
+    a.cap = lists->cap;
+  }
+  hipError_t e = absa::launch_attend_fp8(a, static_cast<hipStream_t>(stream), dense);
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
 
 }  // extern "C"

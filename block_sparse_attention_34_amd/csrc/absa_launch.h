@@ -36,6 +36,40 @@ struct AttendLaunch {
   float scale_log2;  // softmax scale times log2(e)
 };
 
+struct QuantFp8Launch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int BH, L, NK;
+  uint8_t* q8;
+  float* sq;
+  uint8_t* k8;
+  float* sk;
+  float* kbar;
+  uint8_t* v8t;
+  float* sv;
+  uint16_t* mu;
+  double* ksum_part;   // workspace: [BH][ceil(NK/16)][128]
+  float* vmax_part;    // workspace: [BH][ceil(NK/16)][128]
+  uint16_t* mu_nat;    // workspace: [BH][NK][128] bf16
+};
+
+struct AttendFp8Launch {
+  const uint8_t* q8;
+  const float* sq;
+  const uint8_t* k8;
+  const float* sk;
+  const uint8_t* v8t;
+  const float* sv;
+  const uint16_t* mu;
+  const int32_t* count;
+  const int32_t* kv_idx;
+  const float* inv_pi;
+  void* o;
+  int L, NQ, NK, rows, cap, out_bf16;
+  float scale_log2;
+};
+
 // Number of block-range splits of the logit product (and the 32-block tiles per
 // split), chosen so the launch has at least ~2048 workgroups.
 inline int logit_splits(int NQ, int C, int BH, int NKp, int* tiles_per_split) {
@@ -52,5 +86,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st);
 hipError_t configure_select_kernels();
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense);
 hipError_t launch_attend_pp(const AttendLaunch& a, hipStream_t st, bool dense);
+hipError_t launch_quantize_fp8(const QuantFp8Launch& a, hipStream_t st);
+hipError_t launch_attend_fp8(const AttendFp8Launch& a, hipStream_t st, bool dense);
 
 }  // namespace absa

@@ -159,6 +159,70 @@ absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, 
 absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 (E4M3) variant of the attention step.  The VC-Attention page (section
+ * "İki darboğaz") puts most low-bit attention error in the value term, removes
+ * part of it by subtracting a per-block mean of V before quantising, and writes
+ * the softmax probabilities as E4M3 bytes directly, with one fused multiply-add
+ * per element, because an E4M3 byte is close to a scaled log2 of its value
+ * ("ExpCast"); section "Ölçümler" says such a kernel composes with sparse
+ * attention.  The rules implemented here (E4M3 = OCP E4M3FN: bias 7, largest
+ * finite 448; every scale s = 2^e with e the smallest integer for which
+ * max|x| <= 448 s, 1 for all-zero sets):
+ *   Q      per token: s_Q[t] from max_c |q[t][c]|, code = e4m3_rne(q / s_Q);
+ *   K      kbar[c] = fp32(sum_t k[t][c] / L) (mean over the head's L tokens;
+ *          it cancels in every query's softmax); per KV block b:
+ *          s_K[b] from max |k - kbar| over its valid keys, code =
+ *          e4m3_rne((k - kbar) / s_K) with k - kbar rounded to fp32;
+ *   V      mu_hat[b][c] = bf16(fp32(mean of block b's valid keys)); residual
+ *          r = v - mu_hat (fp32); per channel c of the head: s_V[c] from
+ *          max_t |r[t][c]|, code = e4m3_rne(r / s_V);
+ *   P      y = 8 (l - m) + 120 in fp32 with l = scale log2(e) s_Q s_K (q8.k8)
+ *          + log2 w_b and m an integer reference that rises by
+ *          ceil((max y - 120) / 8) whenever a 64-key tile (four list entries,
+ *          in list order) holds a y above 120; p = e4m3 value of the byte
+ *          sat_u8(rne(y));
+ *   O      o_t = sum_k p_k (mu_hat + s_V dec(code_k)) / sum_k p_k (0 for an
+ *          empty list).
+ * Supported shape: d = 128, Bq = 128, Bk = 16.
+ */
+
+/* Quantised operands of one problem; every pointer is a device pointer owned
+ * by the caller, 16-byte aligned.  NK = ceil(L/16). */
+typedef struct absa_fp8_operands {
+  uint8_t* q8;    /* [B,H,L,128]      E4M3 codes of Q                              */
+  float* sq;      /* [B,H,L]          s_Q per token                                */
+  uint8_t* k8;    /* [B,H,L,128]      E4M3 codes of k - kbar                       */
+  float* sk;      /* [B,H,NK]         s_K per KV block                             */
+  float* kbar;    /* [B,H,128]        per-head key mean                            */
+  uint8_t* v8t;   /* [B,H,NK,128,16]  E4M3 codes of v - mu_hat, block by block with
+                                      the 16 keys of a channel contiguous (keys
+                                      past L hold code 0)                          */
+  float* sv;      /* [B,H,128]        s_V per channel                              */
+  uint16_t* mu;   /* [B,H,NK,32,4]    bf16 mu_hat[b][32 j + i] / s_V[32 j + i] at
+                                      [b][i][j], i.e. the four 32-channel groups of
+                                      one lane position contiguous                 */
+} absa_fp8_operands;
+
+/* Bytes of device workspace absa_quantize_fp8 needs ([host] pointers). */
+absa_status absa_fp8_workspace(const absa_problem* prob, size_t* bytes);
+
+/* Quantises bf16 Q, K, V ([B,H,L,128]) into `out` ([host] struct, device
+ * arrays) by the rules above.  workspace: at least absa_fp8_workspace() bytes,
+ * 256-byte aligned, contents on entry ignored.  Returns ABSA_ERR_UNSUPPORTED
+ * unless d = 128 and Bk = 16. */
+absa_status absa_quantize_fp8(const absa_problem* prob, const void* q, const void* k, const void* v,
+                              const absa_fp8_operands* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Block-sparse attention on the quantised operands: the estimate above over
+ * the blocks listed for each row (same list format as absa_attend); with
+ * lists == NULL every key is kept with weight 1 (dense attention in FP8).
+ * o as for absa_attend.  Returns ABSA_ERR_UNSUPPORTED unless d = 128,
+ * Bq = 128 and Bk = 16. */
+absa_status absa_attend_fp8(const absa_problem* prob, const absa_fp8_operands* ops,
+                            const absa_blocklist* lists, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

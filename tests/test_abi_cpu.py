@@ -165,6 +165,38 @@ def test_attend_and_dense_validation(lib):
         _lib.ABSA_ERR_INVALID_ARG
 
 
+def fp8_ops(**kw):
+    base = dict(q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, kbar=FAKE, v8t=FAKE, sv=FAKE, mu=FAKE)
+    base.update(kw)
+    return _lib.AbsaFp8Operands(**base)
+
+
+def test_fp8_validation(lib):
+    P = ctypes.byref(prob(d=128, q_block=128))
+    n = ctypes.c_size_t()
+    assert lib.absa_fp8_workspace(P, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.absa_fp8_workspace(ctypes.byref(prob(d=64)), ctypes.byref(n)) == _lib.ABSA_ERR_UNSUPPORTED
+    assert lib.absa_fp8_workspace(ctypes.byref(prob(d=128, kv_block=32)), ctypes.byref(n)) == \
+        _lib.ABSA_ERR_UNSUPPORTED
+    assert lib.absa_fp8_workspace(P, None) == _lib.ABSA_ERR_INVALID_ARG
+    ws = n.value
+    O = ctypes.byref(fp8_ops())
+    q = lib.absa_quantize_fp8
+    assert q(P, FAKE, FAKE, FAKE, O, FAKE, ws - 1, None) == _lib.ABSA_ERR_WORKSPACE
+    assert q(P, FAKE, FAKE, FAKE, O, None, ws, None) == _lib.ABSA_ERR_WORKSPACE
+    assert q(P, FAKE, FAKE, FAKE, O, FAKE + 16, ws, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert q(P, FAKE, None, FAKE, O, FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert q(P, FAKE, FAKE, FAKE, ctypes.byref(fp8_ops(mu=None)), FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert q(P, FAKE, FAKE, FAKE, ctypes.byref(fp8_ops(sv=FAKE + 4)), FAKE, ws, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert q(P, FAKE, FAKE, FAKE, None, FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    a = lib.absa_attend_fp8
+    assert a(ctypes.byref(prob(d=128, q_block=64)), O, None, FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
+    assert a(P, O, None, None, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert a(P, O, None, FAKE + 8, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert a(P, O, ctypes.byref(lists(cap=0)), FAKE, None) == _lib.ABSA_ERR_SHAPE
+    assert a(P, ctypes.byref(fp8_ops(q8=None)), None, FAKE, None) == _lib.ABSA_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     import block_sparse_attention_34_amd as absa
