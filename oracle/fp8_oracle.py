@@ -44,6 +44,11 @@ F5  ExpCast: p = dec_e4m3(sat_u8(rne(y))), the byte being y rounded to the
     the integer m, so p is a fixed function of l (within 1.0615x of 2^l).
 F6  o_t = sum_k p_k (mu_hat_b(k) + s_V dec(code_k)) / sum_k p_k over the row's
     kept keys (weights through log2 w inside l); an empty list gives 0.
+F7  QK in INT8 instead (the page takes the QK side from earlier low-bit
+    kernels such as SageAttention2, which smooth K and quantise QK to 8-bit
+    integers): the same per-token Q and smoothed per-block K scaling with 127
+    in place of 448 (s = 2^e, e smallest with max |x| <= 127 s), codes
+    clip(rne(x / s), -127, 127); the dot products q8 . k8 are exact integers.
 
 Every fp32 step that decides a code or a byte is taken in fp32 here as in the
 kernel (numpy float32 arithmetic rounds each operation to nearest); the sums
@@ -60,11 +65,12 @@ from .absa_oracle import num_blocks, valid_len
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "pow2_scale",
-    "quantize_q", "smooth_k", "quantize_k", "quantize_v", "Fp8Head",
+    "quantize_q", "smooth_k", "quantize_k", "quantize_v", "Fp8Head", "I8_MAX", "pow2_scale_i8", "i8_encode",
     "quantize_head", "expcast_p", "attend_row_fp8", "attend_all_fp8",
 ]
 
 E4M3_MAX = 448.0
+I8_MAX = 127.0
 EXPCAST_OFFSET = 120.0  # F4: the byte of the reference value 2^0 (a multiple of 8)
 
 _F32 = np.float32
@@ -131,11 +137,28 @@ def pow2_scale(amax) -> np.ndarray:
 _scale = pow2_scale
 
 
+def pow2_scale_i8(amax) -> np.ndarray:
+    """F7: 2^e with e the smallest integer such that amax <= 127 * 2^e (1 where amax == 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, k = np.frexp(amax)                        # 127 = 0.9921875 2^7
+    e = np.where(m <= 0.9921875, k - 7, k - 6)
+    return np.where(amax > 0, np.ldexp(1.0, e), 1.0).astype(_F32)
+
+
+def i8_encode(x) -> np.ndarray:
+    """F7: clip(rne(x), -127, 127) as int8 codes (x already divided by its scale)."""
+    x = np.asarray(x, dtype=_F32).astype(np.float64)
+    return np.clip(np.rint(x), -127, 127).astype(np.int8)
+
+
 # ----------------------------------------------------------------------------- F1-F3
 
-def quantize_q(q: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """F1 for one head: q [L,d] (fp32 values of bf16) -> codes [L,d] uint8, s_Q [L] fp32."""
+def quantize_q(q: np.ndarray, int8: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """F1 (F7) for one head: q [L,d] (fp32 values of bf16) -> codes [L,d] (uint8 E4M3 or int8), s_Q [L]."""
     q = np.asarray(q, dtype=_F32)
+    if int8:
+        s = pow2_scale_i8(np.abs(q).max(axis=1))
+        return i8_encode(q / s[:, None]), s
     s = _scale(np.abs(q).max(axis=1))
     return e4m3_encode(q / s[:, None]), s
 
@@ -146,18 +169,19 @@ def smooth_k(k: np.ndarray) -> np.ndarray:
     return (k.sum(axis=0) / k.shape[0]).astype(_F32)
 
 
-def quantize_k(k: np.ndarray, Bk: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """F2 for one head: k [L,d] -> codes [L,d], s_K [NK] fp32, kbar [d] fp32."""
+def quantize_k(k: np.ndarray, Bk: int, int8: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """F2 (F7) for one head: k [L,d] -> codes [L,d], s_K [NK] fp32, kbar [d] fp32."""
     L = k.shape[0]
     kbar = smooth_k(k)
     kc = np.asarray(k, dtype=_F32) - kbar[None, :]
     NK = num_blocks(L, Bk)
     s = np.empty(NK, dtype=_F32)
-    codes = np.empty(kc.shape, dtype=np.uint8)
+    codes = np.empty(kc.shape, dtype=np.int8 if int8 else np.uint8)
     for b in range(NK):
         t0, t1 = b * Bk, b * Bk + valid_len(b, Bk, L)
-        s[b] = _scale(np.abs(kc[t0:t1]).max())
-        codes[t0:t1] = e4m3_encode(kc[t0:t1] / s[b])
+        amax = np.abs(kc[t0:t1]).max()
+        s[b] = pow2_scale_i8(amax) if int8 else _scale(amax)
+        codes[t0:t1] = i8_encode(kc[t0:t1] / s[b]) if int8 else e4m3_encode(kc[t0:t1] / s[b])
     return codes, s, kbar
 
 
@@ -177,14 +201,19 @@ def quantize_v(v: np.ndarray, Bk: int) -> Tuple[np.ndarray, np.ndarray, np.ndarr
 
 
 class Fp8Head:
-    """F1-F3 of one head: codes, scales and block means."""
+    """F1-F3 (F7 for Q and K with ``qk_int8``) of one head: codes, scales and block means."""
 
-    def __init__(self, q, k, v, Bk: int):
-        self.q8, self.sq = quantize_q(q)
-        self.k8, self.sk, self.kbar = quantize_k(k, Bk)
+    def __init__(self, q, k, v, Bk: int, qk_int8: bool = False):
+        self.qk_int8 = bool(qk_int8)
+        self.q8, self.sq = quantize_q(q, self.qk_int8)
+        self.k8, self.sk, self.kbar = quantize_k(k, Bk, self.qk_int8)
         self.v8, self.sv, self.mu = quantize_v(v, Bk)
         self.Bk = Bk
         self.L = q.shape[0]
+
+    def qk_values(self, codes) -> np.ndarray:
+        """Values of Q or K codes (before their scales) as fp64."""
+        return codes.astype(np.float64) if self.qk_int8 else e4m3_decode(codes)
 
     def values(self) -> np.ndarray:
         """Reconstructed V (F3) as fp64 [L, d]."""
@@ -220,7 +249,7 @@ def attend_row_fp8(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequenc
     L, Bk = hd.L, hd.Bk
     d = hd.q8.shape[1]
     sl2 = _F32(sigma * math.log2(math.e))
-    q8v = e4m3_decode(hd.q8[t0:t0 + n])                      # [n, d] exact
+    q8v = hd.qk_values(hd.q8[t0:t0 + n])                     # [n, d] exact
     qsc = (sl2 * hd.sq[t0:t0 + n]).astype(_F32)              # fp32 per query
     vals = hd.values()
     if dense:
@@ -246,7 +275,7 @@ def attend_row_fp8(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequenc
         if keys.size == 0:
             continue
         blk = keys // Bk
-        acc = q8v @ e4m3_decode(hd.k8[keys]).T               # exact dot products [n, nk]
+        acc = q8v @ hd.qk_values(hd.k8[keys]).T              # exact dot products [n, nk]
         sc8 = (qsc[:, None] * hd.sk[blk][None, :]).astype(_F32) * _F32(8.0)
         m_use = np.where(np.isinf(m), 0.0, m)
         cb = (bias.astype(_F32)[None, :] - m_use.astype(_F32)[:, None]).astype(_F32)
@@ -271,7 +300,7 @@ def attend_row_fp8(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequenc
 
 def attend_all_fp8(q, k, v, Bq: int, Bk: int, count=None, kv_idx=None, inv_pi=None,
                    sigma: Optional[float] = None, dense: bool = False,
-                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+                   rows: Optional[Sequence[int]] = None, qk_int8: bool = False) -> np.ndarray:
     """F1-F6 for the whole problem (or only ``rows``) -> O [B,H,L,d] fp64 (other rows zero)."""
     B, H, L, d = q.shape
     NQ = num_blocks(L, Bq)
@@ -283,7 +312,7 @@ def attend_all_fp8(q, k, v, Bq: int, Bk: int, count=None, kv_idx=None, inv_pi=No
         bh, i = divmod(int(r), NQ)
         b, h = divmod(bh, H)
         if bh not in heads:
-            heads[bh] = Fp8Head(q[b, h], k[b, h], v[b, h], Bk)
+            heads[bh] = Fp8Head(q[b, h], k[b, h], v[b, h], Bk, qk_int8)
         n = valid_len(i, Bq, L)
         if dense:
             o[b, h, i * Bq: i * Bq + n] = attend_row_fp8(heads[bh], i * Bq, n, [], [], sigma, dense=True)

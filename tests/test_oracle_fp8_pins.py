@@ -235,3 +235,44 @@ def test_fp8_close_to_exact_attention_and_empty_list():
     # ~2.6% (P) and ~3% (V) rounding: a relative error of a few percent is the expected size
     assert 0.005 < rel < 0.1
     assert np.all(O.attend_row_fp8(hd, 0, 16, [], [], sigma) == 0.0)
+
+
+# ----------------------------------------------------------------------------- F7 (INT8 QK)
+
+def test_i8_scale_rounding_and_error_bound():
+    rng = np.random.default_rng(8)
+    a = np.exp(rng.uniform(-20, 20, 20000)).astype(np.float32)
+    s = O.pow2_scale_i8(a).astype(np.float64)
+    assert np.all(a <= 127.0 * s) and np.all(a > 63.5 * s)
+    assert O.pow2_scale_i8(np.float32(127.0)) == 1.0 and O.pow2_scale_i8(np.float32(127.5)) == 2.0
+    # ties to even, clamping, exact integers
+    np.testing.assert_array_equal(O.i8_encode(np.float32([0.5, 1.5, 2.5, -2.5, 126.5, 127.4, -300, 7])),
+                                  np.int8([0, 2, 2, -2, 126, 127, -127, 7]))
+    x = rng.standard_normal((64, 32)).astype(np.float32) * 5
+    q8, sq = O.quantize_q(x, int8=True)
+    err = np.abs(q8.astype(np.float64) * sq[:, None] - x)
+    assert np.all(err <= sq[:, None] / 2 * (1 + 1e-7))
+    assert np.all(np.abs(q8).max(axis=1) >= 63)
+
+
+def test_int8_assembly_equals_S6_estimator_on_exact_inputs():
+    rng = np.random.default_rng(9)
+    L, d, Bk = 256, 32, 16
+    q = rng.integers(-127, 128, size=(L, d)) * 2.0 ** -5
+    q[:, 0] = 127 * 2.0 ** -5                                   # per-token max 127 * 2^-5
+    kh = rng.integers(-127, 128, size=(L // 2, d)) * 2.0 ** -6
+    kh[:, 1] = 127 * 2.0 ** -6
+    k = np.concatenate([kh, -kh])                               # exact zero mean
+    v = O.bf16_round(rng.standard_normal((L, d)).astype(np.float32)).astype(np.float64)
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    hd = O.Fp8Head(q, k, v.astype(np.float32), Bk, qk_int8=True)
+    np.testing.assert_array_equal(hd.q8.astype(np.float64) * hd.sq[:, None], q)
+    for b in range(L // Bk):
+        np.testing.assert_array_equal(hd.k8[b * Bk:(b + 1) * Bk].astype(np.float64) * hd.sk[b],
+                                      k[b * Bk:(b + 1) * Bk])
+    sigma = 0.05
+    kept = [3, 0, 9, 15, 4, 7, 12]
+    w = [1.5, 1.0, 3.25, 1.0, 8.0, 2.0, 1.125]
+    got = O.attend_row_fp8(hd, 0, 64, kept, w, sigma, expcast=False)
+    num, den = O.estimator_num_den(q[:64], k, hd.values(), kept, w, Bk, sigma)
+    np.testing.assert_allclose(got, num / den[:, None], rtol=2e-5, atol=2e-5)
