@@ -193,12 +193,13 @@ class Fp8Operands(NamedTuple):
     v8t: "object"   # uint8 [B,H,NK,128,16]
     sv: "object"    # float32 [B,H,128]
     mu: "object"    # int16 (bf16 bits) [B,H,NK,32,4]
+    qk_int8: bool = False  # q8/k8 hold INT8 codes instead of E4M3
 
     def c(self) -> _lib.AbsaFp8Operands:
-        return _lib.AbsaFp8Operands(*(t.data_ptr() for t in self))
+        return _lib.AbsaFp8Operands(*(t.data_ptr() for t in self[:8]), int(bool(self.qk_int8)))
 
 
-def alloc_fp8(prob: Problem, device) -> Fp8Operands:
+def alloc_fp8(prob: Problem, device, qk_int8: bool = False) -> Fp8Operands:
     import torch
     B, H, L, nk = prob.B, prob.H, prob.L, prob.nk
     u8, f32 = torch.uint8, torch.float32
@@ -207,7 +208,7 @@ def alloc_fp8(prob: Problem, device) -> Fp8Operands:
         torch.empty((B, H, L, 128), dtype=u8, device=device), torch.empty((B, H, nk), dtype=f32, device=device),
         torch.empty((B, H, 128), dtype=f32, device=device), torch.empty((B, H, nk, 128, 16), dtype=u8, device=device),
         torch.empty((B, H, 128), dtype=f32, device=device), torch.empty((B, H, nk, 32, 4), dtype=torch.int16,
-                                                                        device=device))
+                                                                        device=device), bool(qk_int8))
 
 
 def fp8_workspace_bytes(prob: Problem) -> int:
@@ -217,11 +218,13 @@ def fp8_workspace_bytes(prob: Problem) -> int:
     return n.value
 
 
-def quantize_fp8(prob: Problem, q, k, v, ops: Optional[Fp8Operands] = None, workspace=None):
-    """E4M3 operands of bf16 Q, K, V (d = 128, Bk = 16).  Returns (ops, workspace)."""
+def quantize_fp8(prob: Problem, q, k, v, ops: Optional[Fp8Operands] = None, workspace=None,
+                 qk_int8: bool = False):
+    """E4M3 operands of bf16 Q, K, V (d = 128, Bk = 16); with ``qk_int8`` Q and K get INT8 codes.
+    Returns (ops, workspace)."""
     import torch
     _check_qkv(prob, q, k, v)
-    ops = alloc_fp8(prob, q.device) if ops is None else ops
+    ops = alloc_fp8(prob, q.device, qk_int8) if ops is None else ops
     nbytes = fp8_workspace_bytes(prob)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

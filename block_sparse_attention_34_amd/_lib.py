@@ -50,6 +50,7 @@ class AbsaFp8Operands(ctypes.Structure):
     _fields_ = [
         ("q8", ctypes.c_void_p), ("sq", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("sk", ctypes.c_void_p),
         ("kbar", ctypes.c_void_p), ("v8t", ctypes.c_void_p), ("sv", ctypes.c_void_p), ("mu", ctypes.c_void_p),
+        ("qk_int8", ctypes.c_int32),
     ]
 
 

@@ -123,6 +123,7 @@ absa_status check_fp8_operands(const absa_fp8_operands* o) {
   const void* ps[] = {o->q8, o->sq, o->k8, o->sk, o->kbar, o->v8t, o->sv, o->mu};
   for (const void* p : ps)
     if (!aligned(p, 16)) return ABSA_ERR_ALIGNMENT;
+  if (o->qk_int8 != 0 && o->qk_int8 != 1) return ABSA_ERR_INVALID_ARG;
   return ABSA_OK;
 }
 
@@ -340,6 +341,7 @@ absa_status absa_quantize_fp8(const absa_problem* prob, const void* q, const voi
   a.BH = (int)dm.BH;
   a.L = prob->L;
   a.NK = dm.NK;
+  a.qk_int8 = out->qk_int8;
   a.q8 = out->q8;
   a.sq = out->sq;
   a.k8 = out->k8;
@@ -383,6 +385,7 @@ absa_status absa_attend_fp8(const absa_problem* prob, const absa_fp8_operands* o
   a.NK = dm.NK;
   a.rows = (int)dm.rows;
   a.out_bf16 = prob->out_bf16;
+  a.qk_int8 = ops->qk_int8;
   const float scale = prob->scale > 0.f ? prob->scale : 1.0f / std::sqrt((float)prob->d);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (!dense) {

@@ -27,6 +27,9 @@
 //   bf16 high and low parts (both in one product: k = 0..3 carry the high
 //   parts, k = 4..7 the low parts).  The per-channel scale s_V multiplies O at
 //   the end.
+//   With INT8 QK (codes clip(rne(x / s), -127, 127), s = 2^e for 127) the QK
+//   product runs on v_mfma_i32_32x32x32_i8 instead (lane l holds k = 16 (l / 32)
+//   + byte), whose int32 dot products are exact.
 //   Logits: y = fma(acc, 8 scale log2(e) s_Q s_K, 8 (log2 w - m) + 120), one
 //   fused multiply-add from the accumulator; P byte = v_cvt_pk_u8_f32(y)
 //   (round to nearest even, clamped to [0, 255]).  The reference m is an
@@ -53,6 +56,19 @@ __device__ __forceinline__ int pow2_exp(float amax) {
   return m <= 0.875f ? k - 9 : k - 8;
 }
 
+// INT8 QK: the smallest e with amax <= 127 * 2^e (0 for amax == 0)
+__device__ __forceinline__ int pow2_exp_i8(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  const float m = frexpf(amax, &k);  // 127 = 0.9921875 2^7
+  return m <= 0.9921875f ? k - 7 : k - 6;
+}
+
+template <bool QI8>
+__device__ __forceinline__ int qk_exp(float amax) {
+  return QI8 ? pow2_exp_i8(amax) : pow2_exp(amax);
+}
+
 __device__ __forceinline__ void unpack8(const u32x4 w, float (&x)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -69,6 +85,23 @@ __device__ __forceinline__ uint32_t codes4(float x0, float x1, float x2, float x
   return (uint32_t)w;
 }
 
+// INT8 codes clip(rne(x * 2^-e), -127, 127) of x[0..3], packed little-endian
+__device__ __forceinline__ uint32_t codes4_i8(float x0, float x1, float x2, float x3, int e) {
+  const float xs[4] = {x0, x1, x2, x3};
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float r = fminf(fmaxf(rintf(ldexpf(xs[i], -e)), -127.f), 127.f);
+    w |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+  }
+  return w;
+}
+
+template <bool QI8>
+__device__ __forceinline__ uint32_t qk_codes4(float x0, float x1, float x2, float x3, int e) {
+  return QI8 ? codes4_i8(x0, x1, x2, x3, e) : codes4(x0, x1, x2, x3, e);
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {  // round to nearest even
   const __bf16 b = (__bf16)x;
   return __builtin_bit_cast(uint16_t, b);
@@ -78,6 +111,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {  // round to nearest ev
 
 // ============================================================================= pre-pass
 // grid (ceil(L/16), BH), 256 threads: 16 tokens per workgroup, 16 lanes per token
+template <bool QI8>
 __global__ __launch_bounds__(256) void fp8_q_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ q8,
                                                     float* __restrict__ sq, int L) {
   const int t = threadIdx.x, cl = t & 15;
@@ -93,9 +127,9 @@ __global__ __launch_bounds__(256) void fp8_q_kernel(const uint16_t* __restrict__
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const int e = pow2_exp(amax);
+  const int e = qk_exp<QI8>(amax);
   if (ok) {
-    const uint32_t c0 = codes4(x[0], x[1], x[2], x[3], e), c1 = codes4(x[4], x[5], x[6], x[7], e);
+    const uint32_t c0 = qk_codes4<QI8>(x[0], x[1], x[2], x[3], e), c1 = qk_codes4<QI8>(x[4], x[5], x[6], x[7], e);
     *reinterpret_cast<uint2*>(q8 + row * FD + 8 * cl) = make_uint2(c0, c1);
     if (cl == 0) sq[row] = ldexpf(1.f, e);
   }
@@ -198,6 +232,7 @@ __global__ __launch_bounds__(128) void fp8_head_kernel(const double* __restrict_
 }
 
 // grid (nchunk, BH), 256 threads; thread (b = t/16, cl = t%16) as in the stats kernel
+template <bool QI8>
 __global__ __launch_bounds__(256) void fp8_kv_quant_kernel(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            const uint16_t* __restrict__ mu_nat,
@@ -248,12 +283,12 @@ __global__ __launch_bounds__(256) void fp8_kv_quant_kernel(const uint16_t* __res
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const int ek = pow2_exp(amax);
+  const int ek = qk_exp<QI8>(amax);
 #pragma unroll
   for (int j = 0; j < FBK; ++j) {
     if (j < n) {
-      const uint32_t c0 = codes4(kc[j][0], kc[j][1], kc[j][2], kc[j][3], ek);
-      const uint32_t c1 = codes4(kc[j][4], kc[j][5], kc[j][6], kc[j][7], ek);
+      const uint32_t c0 = qk_codes4<QI8>(kc[j][0], kc[j][1], kc[j][2], kc[j][3], ek);
+      const uint32_t c1 = qk_codes4<QI8>(kc[j][4], kc[j][5], kc[j][6], kc[j][7], ek);
       *reinterpret_cast<uint2*>(k8 + (bh * L + t0 + j) * FD + 8 * cl) = make_uint2(c0, c1);
     }
   }
@@ -286,7 +321,7 @@ __global__ __launch_bounds__(256) void fp8_kv_quant_kernel(const uint16_t* __res
 }
 
 // ============================================================================= attention
-template <bool DENSE, bool OUT_BF16>
+template <bool DENSE, bool OUT_BF16, bool QI8>
 __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
   constexpr int D = FD, BK = FBK, BQ = 128;
   constexpr int NW = 4;              // waves per row, 32 queries each
@@ -296,6 +331,8 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
   constexpr int VT = SPT * D * BK;   // V tile bytes (8 KB)
   constexpr int MT = SPT * 256;      // block-mean operands of a tile (1 KB)
   typedef int v8i __attribute__((ext_vector_type(8)));
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v16i __attribute__((ext_vector_type(16)));
 
   constexpr int ST = 4 * 256;        // s_K of a tile: each wave lands 64 lanes x 4 B, wave 0's is read
   // one LDS object per slot, the loop unrolled by two: every slot a phase
@@ -352,16 +389,17 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
     }
   }
 
-  // ---- this lane's query as the B operand of S^T = K Q^T: bytes 32 h + 64 ks ..
-  v8i qf[2];
+  // ---- this lane's query as the B operand of S^T = K Q^T: E4M3, two k-steps of
+  // 64 (bytes 64 ks + 32 h ..); INT8, four k-steps of 32 (bytes 32 ks + 16 h ..).
+  // qw[i] is the 16-byte chunk i of the lane's 64 operand bytes.
+  u32x4 qw[4];
   float qs8;  // 8 scale log2(e) s_Q of this query
   {
     const u32x4* qp = reinterpret_cast<const u32x4*>(a.q8 + (head_tok + (qvalid ? qi : 0)) * D);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 w0 = qp[4 * ks + 2 * h], w1 = qp[4 * ks + 2 * h + 1];
-      if (!qvalid) w0 = w1 = u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = v8i{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+    for (int i = 0; i < 4; ++i) {
+      const int c = QI8 ? 2 * i + h : 4 * (i >> 1) + 2 * h + (i & 1);
+      qw[i] = qvalid ? qp[c] : u32x4{0u, 0u, 0u, 0u};
     }
     qs8 = 8.f * a.scale_log2 * (qvalid ? a.sq[head_tok + qi] : 1.f);
   }
@@ -474,17 +512,15 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
   // ---- per-lane LDS read offsets.  QK row i of key half sb holds tile key
   // 32 ((i >> 2) & 1) + 16 sb + 4 (i >> 3) + (i & 3), so that accumulator
   // element r of lane (h, n) in half sb is key 32 h + 16 sb + r.
-  int koff[2][2];  // [ks][chunk pair half] for sb = 0; sb = 1 adds 16 rows
+  int koff[4];  // the four 16-byte chunks of this lane's K operand bytes (as qw), sb = 0; sb = 1 adds 16 rows
   {
     const int i = qn;
     const int r = 32 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = 2 * h + 4 * ks + u;
-        koff[ks][u] = r * D + ((c ^ kswz(r)) << 4);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int c = QI8 ? 2 * j + h : 4 * (j >> 1) + 2 * h + (j & 1);
+      koff[j] = r * D + ((c ^ kswz(r)) << 4);
+    }
   }
   // PV A operand (R^T): lane (h, c) reads channel row 32 cb + c of entries 2h, 2h+1
   const int voff = (2 * h) * (D * BK) + qn * 16;
@@ -505,20 +541,43 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
   v8i pf;  // P bytes of the current tile: byte 16 sb + r = key 32 h + 16 sb + r
   float m_run = -INFINITY, l_run = 0.f;
 
+  // S^T = K Q^T; with INT8 the exact int32 dot products (|acc| <= 127^2 128 < 2^24)
+  // are converted to fp32 exactly
   auto qk = [&](const unsigned char* kb) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.f;
+    if constexpr (QI8) {
+      v16i iacc[2] = {};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(kb + koff[ks][0] + sb * 16 * D);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(kb + koff[ks][1] + sb * 16 * D);
-        const v8i kfrag = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        sacc[sb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kfrag, qf[ks], sacc[sb], 0, 0, 0, 0, 0, 0);
-      }
+        for (int sb = 0; sb < 2; ++sb) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(kb + koff[ks] + sb * 16 * D);
+          const v4i kfrag = {(int)x[0], (int)x[1], (int)x[2], (int)x[3]};
+          const v4i qfrag = {(int)qw[ks][0], (int)qw[ks][1], (int)qw[ks][2], (int)qw[ks][3]};
+          iacc[sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kfrag, qfrag, iacc[sb], 0, 0, 0);
+        }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = (float)iacc[sb][r];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const u32x4 x0 = *reinterpret_cast<const u32x4*>(kb + koff[2 * ks] + sb * 16 * D);
+          const u32x4 x1 = *reinterpret_cast<const u32x4*>(kb + koff[2 * ks + 1] + sb * 16 * D);
+          const v8i kfrag = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                             (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          const v8i qfrag = {(int)qw[2 * ks][0], (int)qw[2 * ks][1], (int)qw[2 * ks][2], (int)qw[2 * ks][3],
+                             (int)qw[2 * ks + 1][0], (int)qw[2 * ks + 1][1], (int)qw[2 * ks + 1][2],
+                             (int)qw[2 * ks + 1][3]};
+          sacc[sb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kfrag, qfrag, sacc[sb], 0, 0, 0, 0, 0, 0);
+        }
+    }
   };
   // O^T += R^T P^T (residual codes) and the block-mean term
   auto pv = [&](const unsigned char* vb) {
@@ -745,24 +804,35 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
 // ============================================================================= launchers
 hipError_t launch_quantize_fp8(const QuantFp8Launch& a, hipStream_t st) {
   const int nchunk = (a.NK + 15) / 16;
-  fp8_q_kernel<<<dim3((a.L + 15) / 16, a.BH), 256, 0, st>>>(a.q, a.q8, a.sq, a.L);
+  if (a.qk_int8) fp8_q_kernel<true><<<dim3((a.L + 15) / 16, a.BH), 256, 0, st>>>(a.q, a.q8, a.sq, a.L);
+  else fp8_q_kernel<false><<<dim3((a.L + 15) / 16, a.BH), 256, 0, st>>>(a.q, a.q8, a.sq, a.L);
   fp8_kv_stats_kernel<<<dim3(nchunk, a.BH), 256, 0, st>>>(a.k, a.v, a.ksum_part, a.vmax_part, a.mu_nat, a.L,
                                                            a.NK);
   fp8_head_kernel<<<dim3(a.BH), 128, 0, st>>>(a.ksum_part, a.vmax_part, a.kbar, a.sv, nchunk, a.L);
-  fp8_kv_quant_kernel<<<dim3(nchunk, a.BH), 256, 0, st>>>(a.k, a.v, a.mu_nat, a.kbar, a.sv, a.k8, a.sk, a.v8t,
-                                                           a.mu, a.L, a.NK);
+  if (a.qk_int8)
+    fp8_kv_quant_kernel<true><<<dim3(nchunk, a.BH), 256, 0, st>>>(a.k, a.v, a.mu_nat, a.kbar, a.sv, a.k8, a.sk,
+                                                                   a.v8t, a.mu, a.L, a.NK);
+  else
+    fp8_kv_quant_kernel<false><<<dim3(nchunk, a.BH), 256, 0, st>>>(a.k, a.v, a.mu_nat, a.kbar, a.sv, a.k8, a.sk,
+                                                                    a.v8t, a.mu, a.L, a.NK);
   return hipGetLastError();
 }
 
-hipError_t launch_attend_fp8(const AttendFp8Launch& a, hipStream_t st, bool dense) {
+template <bool QI8>
+static void launch_attend_fp8_t(const AttendFp8Launch& a, hipStream_t st, bool dense) {
   dim3 grid((a.rows + 1) / 2);
   if (dense) {
-    if (a.out_bf16) attend_fp8_kernel<true, true><<<grid, 512, 0, st>>>(a);
-    else attend_fp8_kernel<true, false><<<grid, 512, 0, st>>>(a);
+    if (a.out_bf16) attend_fp8_kernel<true, true, QI8><<<grid, 512, 0, st>>>(a);
+    else attend_fp8_kernel<true, false, QI8><<<grid, 512, 0, st>>>(a);
   } else {
-    if (a.out_bf16) attend_fp8_kernel<false, true><<<grid, 512, 0, st>>>(a);
-    else attend_fp8_kernel<false, false><<<grid, 512, 0, st>>>(a);
+    if (a.out_bf16) attend_fp8_kernel<false, true, QI8><<<grid, 512, 0, st>>>(a);
+    else attend_fp8_kernel<false, false, QI8><<<grid, 512, 0, st>>>(a);
   }
+}
+
+hipError_t launch_attend_fp8(const AttendFp8Launch& a, hipStream_t st, bool dense) {
+  if (a.qk_int8) launch_attend_fp8_t<true>(a, st, dense);
+  else launch_attend_fp8_t<false>(a, st, dense);
   return hipGetLastError();
 }
 

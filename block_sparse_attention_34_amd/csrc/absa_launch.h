@@ -40,7 +40,7 @@ struct QuantFp8Launch {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  int BH, L, NK;
+  int BH, L, NK, qk_int8;
   uint8_t* q8;
   float* sq;
   uint8_t* k8;
@@ -66,7 +66,7 @@ struct AttendFp8Launch {
   const int32_t* kv_idx;
   const float* inv_pi;
   void* o;
-  int L, NQ, NK, rows, cap, out_bf16;
+  int L, NQ, NK, rows, cap, out_bf16, qk_int8;
   float scale_log2;
 };
 

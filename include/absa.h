@@ -184,6 +184,10 @@ absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, c
  *          sat_u8(rne(y));
  *   O      o_t = sum_k p_k (mu_hat + s_V dec(code_k)) / sum_k p_k (0 for an
  *          empty list).
+ *   QK     optionally INT8 instead of E4M3 (the page builds on earlier 8-bit
+ *          kernels that smooth K and quantise QK to integers): the same Q and
+ *          K scaling with 127 in place of 448, codes clip(rne(x / s), -127, 127),
+ *          exact integer dot products.
  * Supported shape: d = 128, Bq = 128, Bk = 16.
  */
 
@@ -202,6 +206,7 @@ typedef struct absa_fp8_operands {
   uint16_t* mu;   /* [B,H,NK,32,4]    bf16 mu_hat[b][32 j + i] / s_V[32 j + i] at
                                       [b][i][j], i.e. the four 32-channel groups of
                                       one lane position contiguous                 */
+  int32_t qk_int8; /* 0: q8/k8 hold E4M3 codes; 1: INT8 codes (QK below)          */
 } absa_fp8_operands;
 
 /* Bytes of device workspace absa_quantize_fp8 needs ([host] pointers). */

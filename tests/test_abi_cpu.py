@@ -50,9 +50,10 @@ def test_struct_layouts_match_header():
 #include <stddef.h>
 #include "absa.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(absa_problem), offsetof(absa_problem, scale),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(absa_problem), offsetof(absa_problem, scale),
          offsetof(absa_problem, out_bf16), sizeof(absa_select_params),
-         offsetof(absa_select_params, seed), offsetof(absa_select_params, mode), sizeof(absa_blocklist));
+         offsetof(absa_select_params, seed), offsetof(absa_select_params, mode), sizeof(absa_blocklist),
+         sizeof(absa_fp8_operands), offsetof(absa_fp8_operands, qk_int8));
   return 0;
 }
 '''
@@ -64,8 +65,9 @@ int main(void) {
         subprocess.run(["gcc", "-I" + os.path.dirname(HEADER), c, "-o", exe], check=True)
         vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     P, SP, BL = _lib.AbsaProblem, _lib.AbsaSelectParams, _lib.AbsaBlockList
+    F8 = _lib.AbsaFp8Operands
     assert vals == [ctypes.sizeof(P), P.scale.offset, P.out_bf16.offset, ctypes.sizeof(SP), SP.seed.offset,
-                    SP.mode.offset, ctypes.sizeof(BL)]
+                    SP.mode.offset, ctypes.sizeof(BL), ctypes.sizeof(F8), F8.qk_int8.offset]
 
 
 def prob(**kw):
@@ -189,6 +191,7 @@ def test_fp8_validation(lib):
     assert q(P, FAKE, FAKE, FAKE, ctypes.byref(fp8_ops(mu=None)), FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
     assert q(P, FAKE, FAKE, FAKE, ctypes.byref(fp8_ops(sv=FAKE + 4)), FAKE, ws, None) == _lib.ABSA_ERR_ALIGNMENT
     assert q(P, FAKE, FAKE, FAKE, None, FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert q(P, FAKE, FAKE, FAKE, ctypes.byref(fp8_ops(qk_int8=2)), FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
     a = lib.absa_attend_fp8
     assert a(ctypes.byref(prob(d=128, q_block=64)), O, None, FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
     assert a(P, O, None, None, None) == _lib.ABSA_ERR_INVALID_ARG

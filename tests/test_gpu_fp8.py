@@ -63,11 +63,13 @@ def _oracle_mu_op(hd: O.Fp8Head) -> np.ndarray:
 
 def _check_quantisation(ops, wl, heads):
     q8, sq, k8, sk = (t.cpu().numpy() for t in (ops.q8, ops.sq, ops.k8, ops.sk))
+    if ops.qk_int8:
+        q8, k8 = q8.view(np.int8), k8.view(np.int8)
     kbar, v8t, sv = ops.kbar.cpu().numpy(), ops.v8t.cpu().numpy(), ops.sv.cpu().numpy()
     mu = ops.mu.cpu().numpy().view(np.uint16)
     hds = {}
     for h in heads:
-        hd = O.Fp8Head(wl.q[0, h], wl.k[0, h], wl.v[0, h], 16)
+        hd = O.Fp8Head(wl.q[0, h], wl.k[0, h], wl.v[0, h], 16, qk_int8=ops.qk_int8)
         np.testing.assert_array_equal(q8[0, h], hd.q8, err_msg=f"Q codes head {h}")
         np.testing.assert_array_equal(sq[0, h], hd.sq, err_msg=f"s_Q head {h}")
         np.testing.assert_array_equal(kbar[0, h], hd.kbar, err_msg=f"kbar head {h}")
@@ -118,15 +120,16 @@ def _gpu_rows(o, wl, rows, NQ):
 
 # ----------------------------------------------------------------------------- quantisation
 
+@pytest.mark.parametrize("qk_int8", [False, True])
 @pytest.mark.parametrize("shape", [
     dict(H=2, T=3, Hs=7, Ws=9),     # L = 189: ragged last KV block (13 keys) and query block
     dict(H=3, T=4, Hs=16, Ws=20),   # L = 1280
     dict(H=1, T=1, Hs=1, Ws=5),     # L = 5: one partial block
 ])
-def test_quantize_bit_exact(absa, shape):
+def test_quantize_bit_exact(absa, shape, qk_int8):
     wl = _workload(shape["H"], shape["T"], shape["Hs"], shape["Ws"], seed=21, outliers=True)
     p = problem(wl)
-    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v))
+    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v), qk_int8=qk_int8)
     _check_quantisation(ops, wl, range(wl.H))
 
 
@@ -151,15 +154,16 @@ def _to_lists(absa, count, idx, w):
                            torch.from_numpy(w).cuda())
 
 
+@pytest.mark.parametrize("qk_int8", [False, True])
 @pytest.mark.parametrize("shape,keep", [
     (dict(H=2, T=3, Hs=7, Ws=9), 0.5),       # L = 189
     (dict(H=2, T=4, Hs=16, Ws=20), 0.3),     # L = 1280
     (dict(H=1, T=5, Hs=19, Ws=23), 0.15),    # L = 2185, ragged
 ])
-def test_attend_fp8_matches_oracle(absa, shape, keep):
+def test_attend_fp8_matches_oracle(absa, shape, keep, qk_int8):
     wl = _workload(shape["H"], shape["T"], shape["Hs"], shape["Ws"], seed=22)
     p = problem(wl)
-    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v))
+    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v), qk_int8=qk_int8)
     hds = _check_quantisation(ops, wl, range(wl.H))
     rng = np.random.default_rng(5)
     count, idx, w = _random_lists(rng, p.rows, p.nk, keep)
@@ -168,21 +172,22 @@ def test_attend_fp8_matches_oracle(absa, shape, keep):
     ref = _oracle_rows(hds, wl, rows, count, idx, w, p.nq)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 attend {shape} keep {keep}")
+             f"fp8 attend {shape} keep {keep} int8 QK {qk_int8}")
 
 
+@pytest.mark.parametrize("qk_int8", [False, True])
 @pytest.mark.parametrize("shape", [dict(H=2, T=3, Hs=7, Ws=9), dict(H=1, T=4, Hs=16, Ws=20)])
-def test_dense_fp8_matches_oracle(absa, shape):
+def test_dense_fp8_matches_oracle(absa, shape, qk_int8):
     wl = _workload(shape["H"], shape["T"], shape["Hs"], shape["Ws"], seed=23, outliers=True)
     p = problem(wl)
-    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v))
+    ops, _ = absa.quantize_fp8(p, dev(wl.q), dev(wl.k), dev(wl.v), qk_int8=qk_int8)
     hds = _check_quantisation(ops, wl, range(wl.H))
     o = absa.attend_fp8(p, ops, None).cpu().numpy()
     rows = list(range(p.rows))
     ref = _oracle_rows(hds, wl, rows, None, None, None, p.nq, dense=True)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 dense {shape}")
+             f"fp8 dense {shape} int8 QK {qk_int8}")
 
 
 def test_fp8_empty_invalid_and_bf16_output(absa):
@@ -211,13 +216,14 @@ def test_fp8_empty_invalid_and_bf16_output(absa):
     np.testing.assert_allclose(ob.float().cpu().numpy(), o, rtol=2 ** -8, atol=1e-6)
 
 
-def test_fp8_with_sip_lists_wan14b_720p(absa):
+@pytest.mark.parametrize("qk_int8", [False, True])
+def test_fp8_with_sip_lists_wan14b_720p(absa, qk_int8):
     """Full Wan2.1-14B 720p shape: quantisation of two heads bit-exact; attention on sampled rows
     (SIP lists from the library's own selection at keep 9.5%) against the oracle."""
-    wl = gen_config(3)
+    wl = _wan14b()
     p = problem(wl)
     q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
-    ops, _ = absa.quantize_fp8(p, q, k, v)
+    ops, _ = absa.quantize_fp8(p, q, k, v, qk_int8=qk_int8)
     hds = _check_quantisation(ops, wl, [0, wl.H - 1])
     lists, _, _ = absa.select(p, q, k, 0.095, seed=0)
     o = absa.attend_fp8(p, ops, lists).cpu().numpy()
@@ -228,4 +234,13 @@ def test_fp8_with_sip_lists_wan14b_720p(absa):
     ref = _oracle_rows(hds, wl, rows, count, kv_idx, inv_pi, p.nq)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 Wan14B 720p sampled rows ({len(rows)})")
+             f"fp8 Wan14B 720p sampled rows ({len(rows)}) int8 QK {qk_int8}")
+
+
+_WAN14 = {}
+
+
+def _wan14b():
+    if "wl" not in _WAN14:
+        _WAN14["wl"] = gen_config(3)
+    return _WAN14["wl"]
