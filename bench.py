@@ -125,6 +125,27 @@ def ablation(args):
         run("mean query+top-k (prior art)", 64, 0.10, "topk", 0, clusters=1)
         run("mean query+SIP", 64, 0.10, "sip", 0, clusters=1)
 
+        # FP8 path (d = 128, Bk = 16): E4M3 or INT8 QK, ExpCast P and block-mean-centred E4M3 V;
+        # dense (every key) and with the SIP lists at keep 9.5%, seed 0
+        lists = absa.alloc_lists(p16)
+        absa.select(p16, q, k, 0.095, seed=0, lists=lists)
+        o16 = torch.empty_like(o)
+        absa.attend(p16, q, k, v, lists, out=o16)
+        fp8_rows = []
+        for qi8 in (False, True):
+            ops, qws = absa.quantize_fp8(p16, q, k, v, qk_int8=qi8)
+            t_q = timed(lambda: absa.quantize_fp8(p16, q, k, v, ops=ops, workspace=qws))
+            t_d8 = timed(lambda: absa.attend_fp8(p16, ops, None, out=o), n=2)
+            err_d8 = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
+            t_s8 = timed(lambda: absa.attend_fp8(p16, ops, lists, out=o))
+            err_s8 = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
+            err_s8_16 = float(torch.linalg.vector_norm(o - o16) / torch.linalg.vector_norm(o16))
+            fp8_rows.append(("INT8" if qi8 else "E4M3", t_q, t_d8, err_d8, t_s8, err_s8, err_s8_16))
+            print(f"[ablation] temp {temp} fp8 QK {'int8' if qi8 else 'e4m3'}: quantize {t_q:.2f} ms dense "
+                  f"{t_d8:.2f} ms rel-L2 {err_d8:.3e}; SIP 9.5% attend {t_s8:.2f} ms rel-L2 {err_s8:.3e} "
+                  f"(vs bf16 SIP output {err_s8_16:.3e})", file=sys.stderr, flush=True)
+        del ops, qws
+
         print(f"### {'with' if outliers else 'without'} outlier tokens, queries scaled by {temp}: effective keys per query "
               f"{np.mean(eff):.1f}; dense attention {t_dense:.2f} ms "
               f"({dense_flops / (t_dense * 1e-3) / 1e12:.0f} TFLOP/s)\n")
@@ -134,6 +155,12 @@ def ablation(args):
         for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
             print(f"| {label} | {Bk} | {keep:.3f} | {seed} | {C} | {kept:.4f} | {err:.3e} | {ts:.2f} | {ta:.2f} | "
                   f"{dense_flops / ((ts + ta) * 1e-3) / 1e12:.0f} |")
+        print("\nFP8 path (ExpCast E4M3 probabilities, block-mean-centred E4M3 V; Bk 16):\n")
+        print("| QK codes | quantise ms | dense: attend ms | dense: rel-L2 vs bf16 dense | SIP 9.5%: attend ms |"
+              " SIP 9.5%: rel-L2 vs dense | SIP 9.5%: rel-L2 vs bf16 SIP |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for (fmt, tq, td, ed, ts8, es8, es16) in fp8_rows:
+            print(f"| {fmt} | {tq:.2f} | {td:.2f} | {ed:.3e} | {ts8:.2f} | {es8:.3e} | {es16:.3e} |")
         sip = {}
         for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
             if label == "IBCS+SIP" and Bk == 16 and keep in (0.08, 0.095, 0.11):
@@ -314,6 +341,28 @@ def main():
         dms = e0.elapsed_time(e1) / 3
         line["dense_ms"] = dms
         line["dense_mfma_frac"] = dense_flops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        if Bk == 16 and wl.d == 128 and Bq == 128:
+            # the FP8 variant of the attention step on the same lists (not the headline: lower precision)
+            for qi8 in (False, True):
+                ops, qws = absa.quantize_fp8(p, q, k, v, qk_int8=qi8)
+                o8 = torch.empty_like(o)
+                for _ in range(2):
+                    absa.attend_fp8(p, ops, lists, out=o8)
+                e0.record(stream)
+                for _ in range(5):
+                    absa.quantize_fp8(p, q, k, v, ops=ops, workspace=qws)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                tq = e0.elapsed_time(e1) / 5
+                e0.record(stream)
+                for _ in range(5):
+                    absa.attend_fp8(p, ops, lists, out=o8)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                tag = "int8qk" if qi8 else "e4m3"
+                line[f"fp8_{tag}_attend_ms"] = e0.elapsed_time(e1) / 5
+                line[f"fp8_{tag}_quantize_ms"] = tq
+                del ops, qws, o8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.keep, args.kv_block, args.cpu_sample_rows)
     print(json.dumps(line), flush=True)
