@@ -179,9 +179,9 @@ absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, c
  *          max_t |r[t][c]|, code = e4m3_rne(r / s_V);
  *   P      y = 8 (l - m) + 120 in fp32 with l = scale log2(e) s_Q s_K (q8.k8)
  *          + log2 w_b and m an integer reference that rises by
- *          ceil((max y - 120) / 8) whenever a 64-key tile (four list entries,
- *          in list order) holds a y above 120; p = e4m3 value of the byte
- *          sat_u8(rne(y));
+ *          ceil((max y - 120) / 8) + 2 whenever a 64-key tile (four list
+ *          entries, in list order) holds a y above 120; p = e4m3 value of the
+ *          byte sat_u8(rne(y));
  *   O      o_t = sum_k p_k (mu_hat + s_V dec(code_k)) / sum_k p_k (0 for an
  *          empty list).
  *   QK     optionally INT8 instead of E4M3 (the page builds on earlier 8-bit

@@ -37,7 +37,9 @@ F4  Logits in log2 units: y = 8 (l - m) + 120 with l = sigma log2(e) s_Q s_K
     a row are taken in tiles of 64 (four 16-key list entries, in list order;
     the dense case takes consecutive 64-key tiles); whenever a tile holds a y
     above 120 (or on the first tile with a finite logit) m rises by
-    ceil((max y - 120) / 8) and the earlier sums are scaled by 2^-(that step).
+    ceil((max y - 120) / 8) + 2, which leaves the tile's max two octaves below
+    the limit so that the reference moves seldom, and the earlier sums are
+    scaled by 2^-(that step).
 F5  ExpCast: p = dec_e4m3(sat_u8(rne(y))), the byte being y rounded to the
     nearest integer (ties to even) and clamped to [0, 255]; y <= 120 keeps it
     finite.  For bytes in the normal range 2^m dec(byte) does not depend on
@@ -72,6 +74,7 @@ __all__ = [
 E4M3_MAX = 448.0
 I8_MAX = 127.0
 EXPCAST_OFFSET = 120.0  # F4: the byte of the reference value 2^0 (a multiple of 8)
+RESCALE_HEADROOM = 2.0  # F4: octaves left above a tile's max after the reference moves
 
 _F32 = np.float32
 
@@ -283,7 +286,7 @@ def attend_row_fp8(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequenc
         y = (acc * sc8.astype(np.float64) + cb8.astype(np.float64)).astype(_F32).astype(np.float64)
         ymax = y.max(axis=1)
         need = (ymax > EXPCAST_OFFSET) | (np.isinf(m) & np.isfinite(ymax))
-        step = np.where(need, np.ceil((ymax - EXPCAST_OFFSET) / 8.0), 0.0)
+        step = np.where(need, np.ceil((ymax - EXPCAST_OFFSET) / 8.0) + RESCALE_HEADROOM, 0.0)
         alpha = np.where(need & ~np.isinf(m), 2.0 ** -step, np.where(need, 0.0, 1.0))
         num *= alpha[:, None]
         den *= alpha

@@ -8,7 +8,9 @@
   spacing) moves a probability byte across a rounding boundary for roughly 1 element in 10^4; one
   step changes that one weight by ~9%.  Queries without such a flip match the oracle to fp32
   rounding, so the test asks: median per-query relative error <= 1e-4, 99th percentile <= 1e-2,
-  every query <= 0.1, whole output rel-L2 <= 3e-3."""
+  every query <= 0.1, whole output rel-L2 <= 3e-3.  With INT8 QK the dot products are exact
+  integers and y is one fp32 rounding of the same value on both sides (up to the last bit of
+  log2 w), so the bytes agree and the bounds are 1e-4 / 1e-3 / 2e-3 / 1e-3."""
 import math
 import sys
 
@@ -82,8 +84,9 @@ def _check_quantisation(ops, wl, heads):
     return hds
 
 
-def _compare(got: np.ndarray, ref: np.ndarray, what: str):
-    """Whole-output rel-L2 <= 3e-3; per-query relative error: median <= 1e-4, 99% <= 1e-2, all <= 0.1."""
+def _compare(got: np.ndarray, ref: np.ndarray, what: str, int8_qk: bool = False):
+    """E4M3 QK: whole-output rel-L2 <= 3e-3; per-query relative error: median <= 1e-4, 99% <= 1e-2,
+    all <= 0.1.  INT8 QK: 1e-3; 1e-4, 1e-3, 2e-3."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
@@ -94,7 +97,8 @@ def _compare(got: np.ndarray, ref: np.ndarray, what: str):
     p99 = float(np.quantile(qe, 0.99)) if qe.size else 0.0
     qmax = float(qe.max()) if qe.size else 0.0
     _say(what, f"rel_l2={rel:.2e} q50={p50:.2e} q99={p99:.2e} qmax={qmax:.2e}")
-    assert rel <= 3e-3 and p50 <= 1e-4 and p99 <= 1e-2 and qmax <= 0.1, \
+    b_rel, b50, b99, bmax = (1e-3, 1e-4, 1e-3, 2e-3) if int8_qk else (3e-3, 1e-4, 1e-2, 0.1)
+    assert rel <= b_rel and p50 <= b50 and p99 <= b99 and qmax <= bmax, \
         f"{what}: rel_l2={rel:.3e} q50={p50:.3e} q99={p99:.3e} qmax={qmax:.3e}"
 
 
@@ -172,7 +176,7 @@ def test_attend_fp8_matches_oracle(absa, shape, keep, qk_int8):
     ref = _oracle_rows(hds, wl, rows, count, idx, w, p.nq)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 attend {shape} keep {keep} int8 QK {qk_int8}")
+             f"fp8 attend {shape} keep {keep} int8 QK {qk_int8}", qk_int8)
 
 
 @pytest.mark.parametrize("qk_int8", [False, True])
@@ -187,7 +191,7 @@ def test_dense_fp8_matches_oracle(absa, shape, qk_int8):
     ref = _oracle_rows(hds, wl, rows, None, None, None, p.nq, dense=True)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 dense {shape} int8 QK {qk_int8}")
+             f"fp8 dense {shape} int8 QK {qk_int8}", qk_int8)
 
 
 def test_fp8_empty_invalid_and_bf16_output(absa):
@@ -228,13 +232,14 @@ def test_fp8_with_sip_lists_wan14b_720p(absa, qk_int8):
     lists, _, _ = absa.select(p, q, k, 0.095, seed=0)
     o = absa.attend_fp8(p, ops, lists).cpu().numpy()
     count, kv_idx, inv_pi = lists_to_host(lists)
-    rows = [r for r in sample_rows(p.nq, wl.H, 64) if r // p.nq in hds]
-    rows += [0, p.nq - 1, (wl.H - 1) * p.nq, wl.H * p.nq - 1]
+    rng = np.random.default_rng(77)
+    rows = [int(bh) * p.nq + int(i) for bh in hds for i in rng.choice(p.nq, 12, replace=False)]
+    rows += [0, p.nq - 1, (wl.H - 1) * p.nq, wl.H * p.nq - 1]   # first and tail query blocks
     rows = sorted(set(rows))
     ref = _oracle_rows(hds, wl, rows, count, kv_idx, inv_pi, p.nq)
     got = _gpu_rows(o, wl, rows, p.nq)
     _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
-             f"fp8 Wan14B 720p sampled rows ({len(rows)}) int8 QK {qk_int8}")
+             f"fp8 Wan14B 720p sampled rows ({len(rows)}) int8 QK {qk_int8}", qk_int8)
 
 
 _WAN14 = {}
