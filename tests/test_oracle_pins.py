@@ -357,3 +357,70 @@ def test_exact_workload_closed_form(seed):
         pi = O.sip_inclusion(res.scores[r], 16.0)
         assert 0 < (pi == 1).sum() or (pi < 1).all()
     np.testing.assert_array_equal(res.kbar[:, :, :], np.broadcast_to(np.eye(64), (2, 64, 64)))
+
+
+# ----------------------------------------------------------------------------- per-cluster lists (C1-C4)
+
+def test_cluster_scores_mixture_and_normalisation():
+    rng = np.random.default_rng(31)
+    C, NK, d = 4, 37, 16
+    mu = rng.standard_normal((C, d))
+    counts = np.array([5, 0, 9, 2])
+    kbar = rng.standard_normal((NK, d))
+    nk = np.full(NK, 16.0)
+    nk[-1] = 7.0
+    s = O.cluster_scores(mu, counts, kbar, nk, 0.9)
+    np.testing.assert_allclose(s.sum(axis=1), [1, 0, 1, 1], rtol=1e-13)
+    mix = (counts[:, None] / counts.sum() * s).sum(axis=0)
+    np.testing.assert_allclose(mix, O.ibcs_scores(mu, counts, kbar, nk, 0.9), rtol=1e-12, atol=1e-15)
+    # a one-member cluster at a block mean: that block has the largest score
+    mu1 = kbar[[3]] * 5
+    s1 = O.cluster_scores(mu1, np.array([1]), kbar, np.full(NK, 16.0), 1.0)
+    assert np.argmax(s1[0]) == np.argmax(kbar @ mu1[0])
+
+
+def test_one_cluster_equals_shared_selection():
+    wl = gen_micro(3)
+    for mode in (O.SEL_SIP, O.SEL_TOPK):
+        shared = O.select(wl.q, wl.k, wl.q_block, wl.kv_block, 0.3, C=1, mode=mode, seed=5, stream=2)
+        per = O.select_clusters(wl.q, wl.k, wl.q_block, wl.kv_block, 0.3, C=1, mode=mode, seed=5, stream=2)
+        for r_i in range(len(shared.rows)):
+            idx, w, ph = per.lists[r_i][0]
+            np.testing.assert_array_equal(idx, shared.kv_idx[r_i])
+            np.testing.assert_array_equal(w, shared.inv_pi[r_i])
+            np.testing.assert_array_equal(ph, shared.pi_hat[r_i])
+
+
+def test_cluster_streams_differ_and_union_weights():
+    u0 = O.cluster_uniforms(7, 0, 3, 5, 0, 4, 64)
+    u1 = O.cluster_uniforms(7, 0, 3, 5, 1, 4, 64)
+    assert not np.array_equal(u0, u1)
+    np.testing.assert_array_equal(O.cluster_uniforms(7, 0, 3, 20, 1, 4, 64), O.sip_uniforms(7, 0, 3, 81, 64))
+    per = [(np.int32([1, 4, 9]), np.float32([2, 3, 4]), None), (np.int32([]), np.float32([]), None),
+           (np.int32([4, 5]), np.float32([1.5, 8]), None)]
+    blk, W = O.union_lists(per)
+    np.testing.assert_array_equal(blk, [1, 4, 5, 9])
+    np.testing.assert_array_equal(W, np.float32([[2, 0, 0], [3, 0, 1.5], [0, 0, 8], [4, 0, 0]]))
+
+
+def test_cluster_estimator_all_blocks_is_dense_and_members_use_their_list():
+    wl = gen_micro(4)
+    B, H, L, d = wl.q.shape
+    sigma = 1.0 / math.sqrt(d)
+    per = O.select_clusters(wl.q, wl.k, wl.q_block, wl.kv_block, 1.0, C=2, mode=O.SEL_ALL)
+    NQ = O.num_blocks(L, wl.q_block)
+    for r_i, r in enumerate(per.rows):
+        bh, i = divmod(r, NQ)
+        b, h = divmod(bh, H)
+        got = O.attend_row_clusters(wl.q, wl.k, wl.v, bh, i, wl.q_block, wl.kv_block, per.labels[r_i],
+                                    per.lists[r_i], sigma)
+        n = O.valid_len(i, wl.q_block, L)
+        ref = O.dense_rows(wl.q, wl.k, wl.v, bh, i * wl.q_block, i * wl.q_block + n, sigma)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    # hand-made lists: a query of cluster 1 ignores cluster 0's list
+    lab = np.zeros(wl.q_block, dtype=np.int64)
+    lab[3] = 1
+    lists = [(np.int32([0, 1]), np.float32([1, 1]), None), (np.int32([2]), np.float32([4]), None)]
+    got = O.attend_row_clusters(wl.q, wl.k, wl.v, 0, 0, wl.q_block, wl.kv_block, lab, lists, sigma)
+    num, den = O.estimator_num_den(wl.q[0, 0, [3]], wl.k[0, 0], wl.v[0, 0], [2], [4.0], wl.kv_block, sigma)
+    np.testing.assert_allclose(got[3], (num / den[:, None])[0], rtol=1e-12)
