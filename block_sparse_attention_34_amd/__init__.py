@@ -17,6 +17,7 @@ __all__ = [
     "Problem", "BlockLists", "select", "attend", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
     "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
+    "ClusterLists", "alloc_cluster_lists", "select_clusters_workspace_bytes", "select_clusters", "attend_clusters",
 ]
 
 _MODES = {"sip": SEL_SIP, "topk": SEL_TOPK, "all": SEL_ALL}
@@ -248,4 +249,73 @@ def attend_fp8(prob: Problem, ops: Fp8Operands, lists: Optional[BlockLists], out
     st = library().absa_attend_fp8(ctypes.byref(p), ctypes.byref(o), ctypes.byref(bl) if bl is not None else None,
                                    out.data_ptr(), _stream())
     _lib.check(st, "absa_attend_fp8")
+    return out
+
+
+# ----------------------------------------------------------------------------- per-cluster lists
+
+class ClusterLists(NamedTuple):
+    """Per-cluster lists (absa_cluster_lists): the union of a row's cluster samples."""
+    count: "object"   # torch.int32 [rows]
+    kv_idx: "object"  # torch.int32 [rows, cap]
+    w: "object"       # torch.float32 [rows, cap, C]
+    label: "object"   # torch.uint8 [rows, Bq]
+
+    def c(self) -> _lib.AbsaClusterLists:
+        return _lib.AbsaClusterLists(self.count.data_ptr(), self.kv_idx.data_ptr(), self.w.data_ptr(),
+                                     self.label.data_ptr(), int(self.kv_idx.shape[1]), int(self.w.shape[2]))
+
+
+def alloc_cluster_lists(prob: Problem, clusters: int = 4, device="cuda") -> ClusterLists:
+    import torch
+    C = clusters or 4
+    return ClusterLists(torch.zeros(prob.rows, dtype=torch.int32, device=device),
+                        torch.zeros((prob.rows, prob.nk), dtype=torch.int32, device=device),
+                        torch.zeros((prob.rows, prob.nk, C), dtype=torch.float32, device=device),
+                        torch.zeros((prob.rows, prob.q_block), dtype=torch.uint8, device=device))
+
+
+def select_clusters_workspace_bytes(prob: Problem, keep: float, clusters: int = 0, kmeans_steps: int = 0,
+                                    select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0,
+                                    mode="sip") -> int:
+    n = ctypes.c_size_t()
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    _lib.check(library().absa_select_clusters_workspace(ctypes.byref(p), ctypes.byref(sp), ctypes.byref(n)),
+               "absa_select_clusters_workspace")
+    return n.value
+
+
+def select_clusters(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmeans_steps: int = 0,
+                    select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0, mode="sip",
+                    lists: Optional[ClusterLists] = None, workspace=None):
+    """IBCS + one SIP (or TOPK / ALL) sample per cluster.  Returns (lists, workspace)."""
+    import torch
+    _check_qkv(prob, q, k)
+    lists = alloc_cluster_lists(prob, clusters, q.device) if lists is None else lists
+    nbytes = select_clusters_workspace_bytes(prob, keep, clusters, kmeans_steps, select_scale_log2, seed,
+                                             stream_id, mode)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    cl = lists.c()
+    st = library().absa_select_clusters(ctypes.byref(p), ctypes.byref(sp), q.data_ptr(), k.data_ptr(),
+                                        ctypes.byref(cl), workspace.data_ptr(), workspace.numel(), _stream())
+    _lib.check(st, "absa_select_clusters")
+    return lists, workspace
+
+
+def attend_clusters(prob: Problem, q, k, v, lists: ClusterLists, out=None):
+    """Attention over per-cluster lists (each query over its cluster's sample).  Returns O."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    p = prob.c()
+    cl = lists.c()
+    st = library().absa_attend_clusters(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        ctypes.byref(cl), out.data_ptr(), _stream())
+    _lib.check(st, "absa_attend_clusters")
     return out

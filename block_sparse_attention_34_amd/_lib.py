@@ -19,6 +19,7 @@ EXPORTED = (
     "absa_version", "absa_status_string", "absa_num_blocks", "absa_select_workspace",
     "absa_select_workspace_layout", "absa_select", "absa_attend", "absa_dense",
     "absa_fp8_workspace", "absa_quantize_fp8", "absa_attend_fp8",
+    "absa_select_clusters_workspace", "absa_select_clusters", "absa_attend_clusters",
 )
 
 
@@ -43,6 +44,13 @@ class AbsaBlockList(ctypes.Structure):
     _fields_ = [
         ("count", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("inv_pi", ctypes.c_void_p),
         ("cap", ctypes.c_int32),
+    ]
+
+
+class AbsaClusterLists(ctypes.Structure):
+    _fields_ = [
+        ("count", ctypes.c_void_p), ("kv_idx", ctypes.c_void_p), ("w", ctypes.c_void_p),
+        ("label", ctypes.c_void_p), ("cap", ctypes.c_int32), ("clusters", ctypes.c_int32),
     ]
 
 
@@ -90,6 +98,13 @@ def load() -> ctypes.CDLL:
     lib.absa_attend.argtypes = [P, vp, vp, vp, BL, vp, vp]
     lib.absa_dense.restype = ctypes.c_int
     lib.absa_dense.argtypes = [P, vp, vp, vp, vp, vp]
+    CL = ctypes.POINTER(AbsaClusterLists)
+    lib.absa_select_clusters_workspace.restype = ctypes.c_int
+    lib.absa_select_clusters_workspace.argtypes = [P, SP, ctypes.POINTER(sz)]
+    lib.absa_select_clusters.restype = ctypes.c_int
+    lib.absa_select_clusters.argtypes = [P, SP, vp, vp, CL, vp, sz, vp]
+    lib.absa_attend_clusters.restype = ctypes.c_int
+    lib.absa_attend_clusters.argtypes = [P, vp, vp, vp, CL, vp, vp]
     F8 = ctypes.POINTER(AbsaFp8Operands)
     lib.absa_fp8_workspace.restype = ctypes.c_int
     lib.absa_fp8_workspace.argtypes = [P, ctypes.POINTER(sz)]

@@ -98,6 +98,38 @@ WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
   return w;
 }
 
+// per-cluster selection: the standard regions with scores for every (row, cluster),
+// then the clusters' own lists [rows * C][NK] (count, index, weight)
+struct WsClusters {
+  WsLayout base;
+  size_t ccount, cidx, cw, total;
+};
+
+WsClusters ws_layout_clusters(const absa_problem* p, const Dims& dm, int C) {
+  WsClusters w;
+  w.base = ws_layout(p, dm, C);
+  size_t o = w.base.total;
+  // the score region (offset 3) grows from [rows][NK] to [rows * C][NK]: give it a new home at the end
+  w.base.off[3] = o;
+  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
+  w.ccount = o;
+  o = align_up(o + (size_t)dm.rows * C * sizeof(int32_t), kWsAlign);
+  w.cidx = o;
+  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(int32_t), kWsAlign);
+  w.cw = o;
+  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
+  w.total = o;
+  return w;
+}
+
+absa_status check_cluster_lists(const absa_cluster_lists* l, int NK, int C) {
+  if (!l || !l->count || !l->kv_idx || !l->w || !l->label) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(l->count, 4) || !aligned(l->kv_idx, 4) || !aligned(l->w, 4)) return ABSA_ERR_ALIGNMENT;
+  if (l->cap < NK) return ABSA_ERR_SHAPE;
+  if (l->clusters != C) return ABSA_ERR_SHAPE;
+  return ABSA_OK;
+}
+
 absa_status check_lists(const absa_blocklist* l, bool need_cap_nk, int NK) {
   if (!l || !l->count || !l->kv_idx || !l->inv_pi) return ABSA_ERR_INVALID_ARG;
   if (!aligned(l->count, 4) || !aligned(l->kv_idx, 4) || !aligned(l->inv_pi, 4)) return ABSA_ERR_ALIGNMENT;
@@ -204,6 +236,41 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
   return ABSA_OK;
 }
 
+static absa::SelectLaunch select_launch(const absa_problem* prob, const absa_select_params* params,
+                                        const Dims& dm, const SelParams& sp, const WsLayout& w, char* ws,
+                                        const void* q, const void* k) {
+  absa::SelectLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.B = prob->B;
+  a.H = prob->H;
+  a.L = prob->L;
+  a.d = prob->d;
+  a.Bq = prob->q_block;
+  a.Bk = prob->kv_block;
+  a.NQ = dm.NQ;
+  a.NK = dm.NK;
+  a.NKp = dm.NKp;
+  a.C = sp.C;
+  a.Tk = sp.Tk;
+  a.mode = sp.mode;
+  const double nstar = (double)sp.keep * (double)dm.NK;
+  a.nstar = (float)nstar;
+  const double kst = std::floor(nstar + 0.5);
+  a.kstar = (int)(kst < (double)dm.NK ? kst : (double)dm.NK);
+  a.alpha = sp.alpha;
+  a.key0 = (uint32_t)(params->seed & 0xFFFFFFFFull);
+  a.key1 = (uint32_t)(params->seed >> 32);
+  a.ctr3 = params->stream;
+  a.kbarT = reinterpret_cast<float*>(ws + w.off[0]);
+  a.mu = reinterpret_cast<float*>(ws + w.off[1]);
+  a.nj = reinterpret_cast<int*>(ws + w.off[2]);
+  a.s = reinterpret_cast<float*>(ws + w.off[3]);
+  a.logit = reinterpret_cast<float*>(ws + w.off[4]);
+  a.mz = reinterpret_cast<float2*>(ws + w.off[5]);
+  return a;
+}
+
 absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
                         const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
@@ -226,41 +293,63 @@ absa_status absa_select(const absa_problem* prob, const absa_select_params* para
   std::call_once(g_attr_once, [] { g_attr_err = absa::configure_select_kernels(); });
   if (g_attr_err != hipSuccess) return ABSA_ERR_HIP;
 
-  char* ws = static_cast<char*>(workspace);
-  absa::SelectLaunch a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.B = prob->B;
-  a.H = prob->H;
-  a.L = prob->L;
-  a.d = prob->d;
-  a.Bq = prob->q_block;
-  a.Bk = prob->kv_block;
-  a.NQ = dm.NQ;
-  a.NK = dm.NK;
-  a.NKp = dm.NKp;
-  a.C = sp.C;
-  a.Tk = sp.Tk;
-  a.mode = sp.mode;
-  const double nstar = (double)sp.keep * (double)dm.NK;
-  a.nstar = (float)nstar;
-  const double kst = std::floor(nstar + 0.5);
-  a.kstar = (int)(kst < (double)dm.NK ? kst : (double)dm.NK);
-  a.cap = out->cap;
-  a.alpha = sp.alpha;
-  a.key0 = (uint32_t)(params->seed & 0xFFFFFFFFull);
-  a.key1 = (uint32_t)(params->seed >> 32);
-  a.ctr3 = params->stream;
-  a.kbarT = reinterpret_cast<float*>(ws + w.off[0]);
-  a.mu = reinterpret_cast<float*>(ws + w.off[1]);
-  a.nj = reinterpret_cast<int*>(ws + w.off[2]);
-  a.s = reinterpret_cast<float*>(ws + w.off[3]);
-  a.logit = reinterpret_cast<float*>(ws + w.off[4]);
-  a.mz = reinterpret_cast<float2*>(ws + w.off[5]);
+  absa::SelectLaunch a = select_launch(prob, params, dm, sp, w, static_cast<char*>(workspace), q, k);
   a.count = out->count;
   a.kv_idx = out->kv_idx;
   a.inv_pi = out->inv_pi;
+  a.cap = out->cap;
   a.pi_out = pi_out;
+  hipError_t e = absa::launch_select(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
+absa_status absa_select_clusters_workspace(const absa_problem* prob, const absa_select_params* params,
+                                           size_t* bytes) {
+  if (!bytes) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  SelParams sp;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  st = check_params(prob, params, &sp);
+  if (st != ABSA_OK) return st;
+  *bytes = ws_layout_clusters(prob, dm, sp.C).total;
+  return ABSA_OK;
+}
+
+absa_status absa_select_clusters(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                 const void* k, const absa_cluster_lists* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Dims dm;
+  SelParams sp;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  st = check_params(prob, params, &sp);
+  if (st != ABSA_OK) return st;
+  if (!q || !k) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16)) return ABSA_ERR_ALIGNMENT;
+  if (dm.NK > kMaxNK) return ABSA_ERR_UNSUPPORTED;
+  st = check_cluster_lists(out, dm.NK, sp.C);
+  if (st != ABSA_OK) return st;
+  const WsClusters w = ws_layout_clusters(prob, dm, sp.C);
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+
+  std::call_once(g_attr_once, [] { g_attr_err = absa::configure_select_kernels(); });
+  if (g_attr_err != hipSuccess) return ABSA_ERR_HIP;
+
+  char* ws = static_cast<char*>(workspace);
+  absa::SelectLaunch a = select_launch(prob, params, dm, sp, w.base, ws, q, k);
+  a.per_cluster = 1;
+  a.count = reinterpret_cast<int32_t*>(ws + w.ccount);
+  a.kv_idx = reinterpret_cast<int32_t*>(ws + w.cidx);
+  a.inv_pi = reinterpret_cast<float*>(ws + w.cw);
+  a.cap = dm.NK;
+  a.pi_out = nullptr;
+  a.label = out->label;
+  a.ucount = out->count;
+  a.uidx = out->kv_idx;
+  a.uw = out->w;
+  a.ucap = out->cap;
   hipError_t e = absa::launch_select(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
@@ -309,6 +398,45 @@ absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, 
 absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
                        void* stream) {
   return attend_common(prob, q, k, v, nullptr, o, stream, true);
+}
+
+absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const void* k, const void* v,
+                                 const absa_cluster_lists* lists, void* o, void* stream) {
+  Dims dm;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  if (!q || !k || !v || !o) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
+  if (prob->q_block != 128) return ABSA_ERR_UNSUPPORTED;
+  if (!lists) return ABSA_ERR_INVALID_ARG;
+  if (lists->clusters != 1 && lists->clusters != 2 && lists->clusters != 4 && lists->clusters != 8)
+    return ABSA_ERR_UNSUPPORTED;
+  st = check_cluster_lists(lists, dm.NK, lists->clusters);
+  if (st != ABSA_OK) return st;
+  absa::AttendLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.L = prob->L;
+  a.d = prob->d;
+  a.Bq = prob->q_block;
+  a.Bk = prob->kv_block;
+  a.NQ = dm.NQ;
+  a.NK = dm.NK;
+  a.rows = (int)dm.rows;
+  a.out_bf16 = prob->out_bf16;
+  const float scale = prob->scale > 0.f ? prob->scale : 1.0f / std::sqrt((float)prob->d);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.count = lists->count;
+  a.kv_idx = lists->kv_idx;
+  a.inv_pi = nullptr;
+  a.cap = lists->cap;
+  a.wc = lists->w;
+  a.label = lists->label;
+  a.C = lists->clusters;
+  hipError_t e = absa::launch_attend(a, static_cast<hipStream_t>(stream), false);
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
 
 absa_status absa_fp8_workspace(const absa_problem* prob, size_t* bytes) {

@@ -33,7 +33,7 @@
 
 namespace absa {
 
-template <int D, int BK, bool DENSE, bool OUT_BF16>
+template <int D, int BK, bool DENSE, bool OUT_BF16, bool PC>
 __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   constexpr int BQ = 128;
   constexpr int HT = 256;              // threads per row
@@ -121,7 +121,13 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     }
   }
   const int32_t* lidx = DENSE ? nullptr : a.kv_idx + (size_t)rowc * a.cap;
-  const float* lw = DENSE ? nullptr : a.inv_pi + (size_t)rowc * a.cap;
+  const float* lw = (DENSE || PC) ? nullptr : a.inv_pi + (size_t)rowc * a.cap;
+  // Per-cluster lists: the row's list is the union of its clusters' samples;
+  // lane l decodes entry l % SPT for cluster (l / SPT) % C, and each query takes
+  // the bias of its own cluster (-inf where that cluster did not draw the block)
+  const float* lwc = PC ? a.wc + (size_t)rowc * a.cap * a.C : nullptr;
+  const int ccl = PC ? (lane / SPT) % a.C : 0;
+  const int cq = PC ? (int)a.label[(size_t)rowc * BQ + wq * 32 + qn] : 0;
 
   // ---- direct loads (as in the one-row kernel): buffer resources cover this
   // head's K and V (L*D*2 bytes); rows past L lie past the end of the resource
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
       const int e = tile * SPT + lane % SPT;
       const int ec = e < last ? e : last;
       E.blk = lidx[ec];
-      E.w = lw[ec];
+      E.w = PC ? lwc[(size_t)ec * a.C + ccl] : lw[ec];
     }
   };
   // A decoded tile: the wave-uniform byte base of each wave-wide load, the
@@ -269,8 +275,12 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   auto logits = [&](const Tile& tl, float m_use) {
     float cb[SPT];
 #pragma unroll
-    for (int i = 0; i < SPT; ++i)
-      cb[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tl.bias), i)) - m_use;
+    for (int i = 0; i < SPT; ++i) {
+      if constexpr (PC)
+        cb[i] = __shfl(tl.bias, SPT * cq + i, 64) - m_use;
+      else
+        cb[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tl.bias), i)) - m_use;
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -501,10 +511,19 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
 template <int D, int BK, bool DENSE>
 static hipError_t launch_pp_t(const AttendLaunch& a, hipStream_t st) {
   dim3 grid((a.rows + 1) / 2);
+  if constexpr (!DENSE) {
+    if (a.wc) {
+      if (a.out_bf16)
+        attend_pp_kernel<D, BK, false, true, true><<<grid, 512, 0, st>>>(a);
+      else
+        attend_pp_kernel<D, BK, false, false, true><<<grid, 512, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (a.out_bf16)
-    attend_pp_kernel<D, BK, DENSE, true><<<grid, 512, 0, st>>>(a);
+    attend_pp_kernel<D, BK, DENSE, true, false><<<grid, 512, 0, st>>>(a);
   else
-    attend_pp_kernel<D, BK, DENSE, false><<<grid, 512, 0, st>>>(a);
+    attend_pp_kernel<D, BK, DENSE, false, false><<<grid, 512, 0, st>>>(a);
   return hipGetLastError();
 }
 

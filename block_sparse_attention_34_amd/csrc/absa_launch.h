@@ -22,6 +22,14 @@ struct SelectLaunch {
   int32_t* kv_idx;
   float* inv_pi;
   float* pi_out;  // may be null
+  // per-cluster lists: count / kv_idx / inv_pi above are then the workspace lists
+  // [rows * C][cap], and the union goes to ucount / uidx / uw
+  int per_cluster;
+  uint8_t* label;  // [rows][Bq] last k-means assignment, may be null
+  int32_t* ucount;
+  int32_t* uidx;
+  float* uw;
+  int ucap;
 };
 
 struct AttendLaunch {
@@ -34,6 +42,11 @@ struct AttendLaunch {
   void* o;
   int L, d, Bq, Bk, NQ, NK, rows, cap, out_bf16;
   float scale_log2;  // softmax scale times log2(e)
+  // per-cluster lists (null wc: one list per row): kv_idx is the union, wc[row][cap][C]
+  // the per-cluster weights, label[row][Bq] each query's cluster
+  const float* wc;
+  const uint8_t* label;
+  int C;
 };
 
 struct QuantFp8Launch {

@@ -100,7 +100,8 @@ __device__ __forceinline__ int xq_off(int q, int c) {  // byte offset of 16-byte
 template <int D, int C>
 __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* __restrict__ q,
                                                                float* __restrict__ mu_out,
-                                                               int* __restrict__ nj_out, int L, int Bq,
+                                                               int* __restrict__ nj_out,
+                                                               uint8_t* __restrict__ lab_out, int L, int Bq,
                                                                int NQ, int Tk) {
   constexpr int KS = D / 16;   // k-steps of the assignment product
   constexpr int CH = D / 8;    // 16-byte chunks per row
@@ -255,6 +256,8 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
   float* mo = mu_out + (size_t)row * C * D;
   for (int idx = t; idx < C * D; idx += 256) mo[idx] = mu_s[idx / D][idx % D];
   if (t < C) nj_out[(size_t)row * C + t] = cnt[t];
+  // the last assignment of each query (per-cluster lists), 0 past the block's queries
+  if (lab_out && t < Bq) lab_out[(size_t)row * Bq + t] = (uint8_t)(t < n ? lab[t] : 0);
 }
 
 // ============================================================================= K2b
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
                                                      int32_t* __restrict__ count_out,
                                                      int32_t* __restrict__ kv_idx,
                                                      float* __restrict__ inv_pi, int cap,
-                                                     float* __restrict__ pi_out) {
+                                                     float* __restrict__ pi_out, int per_cluster) {
   extern __shared__ float s[];                      // [NK]
   unsigned char* flag = reinterpret_cast<unsigned char*>(s + NK);  // [NK]
   __shared__ float redf[2 * (SIP_NT / 64)];
@@ -454,6 +457,15 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
   const int t = threadIdx.x;
   const int row = blockIdx.x;
   const int bh = row / NQ, i = row % NQ;
+  // Per-cluster lists: workgroup (row, j) samples cluster j alone (its own block
+  // distribution, the full budget, Philox counter word i C + j) into list row C + j;
+  // a cluster without members gets an empty list.
+  const int jsel = per_cluster ? (int)blockIdx.y : -1;
+  const int orow = per_cluster ? row * C + jsel : row;
+  if (per_cluster && nj[(size_t)row * C + jsel] == 0) {
+    if (t == 0) count_out[orow] = 0;
+    return;
+  }
 
   // ---- IBCS scores of this row from its logits: per centroid the max m_j and
   // the normaliser Z_j = sum_b nk_b 2^(l_jb - m_j) (terms below 2^-64 of the
@@ -474,14 +486,17 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
       const int n = min(Bq, L - i * Bq);
       const int cnt = nj[(size_t)row * C + t];
       mj_s[t] = m;
-      coef_s[t] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), zs) : 0.f;
+      if (per_cluster)
+        coef_s[t] = (t == jsel) ? __fdiv_rn(1.f, zs) : 0.f;
+      else
+        coef_s[t] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), zs) : 0.f;
     }
     __syncthreads();
     float mj[C], coef[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) { mj[j] = mj_s[j]; coef[j] = coef_s[j]; }
     constexpr int U = 4;  // blocks per batch: U*C loads in flight
-    float* srow_out = s_out + (size_t)row * NK;
+    float* srow_out = s_out + (size_t)orow * NK;
 #pragma unroll 1
     for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
       float lv[U][C];
@@ -564,7 +579,8 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
   int nkept = 0;
   for (int g = b0; g < b1; g += 4) {
     philox_u4 x = {0u, 0u, 0u, 0u};
-    if (mode == 0) x = philox4x32_10({(uint32_t)(g >> 2), (uint32_t)i, (uint32_t)bh, ctr3}, key0, key1);
+    const uint32_t ctr1 = per_cluster ? (uint32_t)(i * C + jsel) : (uint32_t)i;
+    if (mode == 0) x = philox4x32_10({(uint32_t)(g >> 2), ctr1, (uint32_t)bh, ctr3}, key0, key1);
     const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -589,8 +605,8 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
   }
   int total;
   int off = block_exclusive_scan<SIP_NT>(nkept, redi, total);
-  int32_t* idx_row = kv_idx + (size_t)row * cap;
-  float* w_row = inv_pi + (size_t)row * cap;
+  int32_t* idx_row = kv_idx + (size_t)orow * cap;
+  float* w_row = inv_pi + (size_t)orow * cap;
   for (int b = b0; b < b1; ++b) {
     if (flag[b] == 3) {
       idx_row[off] = b;
@@ -598,7 +614,63 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
       ++off;
     }
   }
-  if (t == 0) count_out[row] = total;
+  if (t == 0) count_out[orow] = total;
+}
+
+// ============================================================================= per-cluster union
+// One workgroup per row: the ascending union of the row's C cluster lists and
+// the weight of every (entry, cluster) pair, 0 where the cluster did not draw
+// the block.  LDS holds one word per KV block: the cluster mask in the low 8
+// bits, the union position above it.
+__global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __restrict__ ccount,
+                                                               const int32_t* __restrict__ cidx,
+                                                               const float* __restrict__ cw, int ccap, int C,
+                                                               int NK, int32_t* __restrict__ ucount,
+                                                               int32_t* __restrict__ uidx, float* __restrict__ uw,
+                                                               int ucap) {
+  extern __shared__ uint32_t slot[];  // [NK]
+  __shared__ int redi[2 * (SIP_NT / 64)];
+  const int t = threadIdx.x;
+  const size_t row = blockIdx.x;
+  for (int b = t; b < NK; b += SIP_NT) slot[b] = 0u;
+  __syncthreads();
+  for (int j = 0; j < C; ++j) {
+    const int n = min(ccount[row * C + j], ccap);
+    const int32_t* li = cidx + (row * C + j) * ccap;
+    for (int e = t; e < n; e += SIP_NT) {
+      const int b = li[e];
+      if ((unsigned)b < (unsigned)NK) atomicOr(&slot[b], 1u << j);
+    }
+  }
+  __syncthreads();
+  const int P = (NK + SIP_NT - 1) / SIP_NT;  // contiguous chunk of blocks per thread
+  const int b0 = min(NK, t * P), b1 = min(NK, b0 + P);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += slot[b] != 0u;
+  int total;
+  int pos = block_exclusive_scan<SIP_NT>(mine, redi, total);
+  float* wrow = uw + row * ucap * C;
+  for (int b = b0; b < b1; ++b) {
+    const uint32_t m = slot[b];
+    if (m) {
+      uidx[row * ucap + pos] = b;
+      for (int j = 0; j < C; ++j)
+        if (!((m >> j) & 1u)) wrow[(size_t)pos * C + j] = 0.f;  // the drawn ones are written below
+      slot[b] = ((uint32_t)pos << 8) | m;
+      ++pos;
+    }
+  }
+  __syncthreads();
+  for (int j = 0; j < C; ++j) {
+    const int n = min(ccount[row * C + j], ccap);
+    const int32_t* li = cidx + (row * C + j) * ccap;
+    const float* lw = cw + (row * C + j) * ccap;
+    for (int e = t; e < n; e += SIP_NT) {
+      const int b = li[e];
+      if ((unsigned)b < (unsigned)NK) wrow[(size_t)(slot[b] >> 8) * C + j] = lw[e];
+    }
+  }
+  if (t == 0) ucount[row] = total;
 }
 
 // ============================================================================= launchers
@@ -618,7 +690,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   // K2a
   {
 #define ABSA_KM(DD, CC) \
-  ibcs_kmeans_mfma_kernel<DD, CC><<<rows, 256, 0, st>>>(a.q, a.mu, a.nj, a.L, a.Bq, a.NQ, a.Tk)
+  ibcs_kmeans_mfma_kernel<DD, CC><<<rows, 256, 0, st>>>(a.q, a.mu, a.nj, a.label, a.L, a.Bq, a.NQ, a.Tk)
     if (a.d == 128) {
       switch (a.C) {
         case 1: ABSA_KM(128, 1); break;
@@ -659,11 +731,12 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     int per;
     const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
     const size_t lds = (size_t)a.NK * (sizeof(float) + 1);
-#define ABSA_SIP(CC)                                                                                  \
-  sip_kernel<CC><<<rows, SIP_NT, lds, st>>>(a.logit, a.mz, nsplit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK,  \
-                                            a.NQ, a.nstar,                                              \
-                                            a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
-                                            a.inv_pi, a.cap, a.pi_out)
+    const dim3 sgrid(rows, a.per_cluster ? a.C : 1);
+#define ABSA_SIP(CC)                                                                                   \
+  sip_kernel<CC><<<sgrid, SIP_NT, lds, st>>>(a.logit, a.mz, nsplit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK,  \
+                                             a.NQ, a.nstar,                                              \
+                                             a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
+                                             a.inv_pi, a.cap, a.pi_out, a.per_cluster)
     switch (a.C) {
       case 1: ABSA_SIP(1); break;
       case 2: ABSA_SIP(2); break;
@@ -671,6 +744,13 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
       default: ABSA_SIP(8); break;
     }
 #undef ABSA_SIP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // union of the per-cluster lists
+  if (a.per_cluster) {
+    cluster_union_kernel<<<rows, SIP_NT, (size_t)a.NK * sizeof(uint32_t), st>>>(
+        a.count, a.kv_idx, a.inv_pi, a.cap, a.C, a.NK, a.ucount, a.uidx, a.uw, a.ucap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -160,6 +160,49 @@ absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, c
                        void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Per-cluster block lists.  The PIVOT page (section "PIVOT'un arkasındaki iki
+ * gözlem") scores one proxy per group of queries and then refines the proxy's
+ * candidate list for each member of the group; here the groups are the IBCS
+ * clusters of each query block and the refinement is one SIP sample per
+ * cluster:
+ *   score      s_b^(j) = nk_b 2^(l_jb - m_j) / Z_j (cluster j's own block
+ *              distribution; the shared score is the mixture over j);
+ *   sample     per cluster: capped pi^(j) with sum = keep * NK, Philox counter
+ *              (b/4, i*C + j, b*H+h, stream), weight fp32(1/pi); a cluster with
+ *              no member gets an empty list (TOPK and ALL modes likewise per
+ *              cluster);
+ *   estimate   each query over its own cluster's list and weights.
+ * With C = 1 the sample equals the shared one.  Attention walks the union of a
+ * row's lists once, in the 128-query two-row kernel (Bq = 128). */
+typedef struct absa_cluster_lists {
+  int32_t* count;   /* [rows]             entries in the row's union list                */
+  int32_t* kv_idx;  /* [rows][cap]        ascending union of the clusters' samples       */
+  float* w;         /* [rows][cap][C]     weight of entry e for cluster j, 0 if cluster j
+                                          did not draw the block                         */
+  uint8_t* label;   /* [rows][Bq]         cluster of each query of the row (the last
+                                          k-means assignment; 0 past the block's queries) */
+  int32_t cap;      /* >= NK                                                             */
+  int32_t clusters; /* C; must equal the selection's cluster count                       */
+} absa_cluster_lists;
+
+/* Bytes of device workspace absa_select_clusters needs ([host] pointers). */
+absa_status absa_select_clusters_workspace(const absa_problem* prob, const absa_select_params* params,
+                                           size_t* bytes);
+
+/* Per-cluster selection into `out` ([host] struct, device arrays, 4-byte
+ * aligned).  Same requirements and workspace rules as absa_select (NK <=
+ * 12288); the workspace is larger (scores and lists of every cluster). */
+absa_status absa_select_clusters(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                 const void* k, const absa_cluster_lists* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Attention over per-cluster lists: query t of row r over the blocks its
+ * cluster drew, with that cluster's weights.  Layouts as for absa_attend;
+ * requires Bq = 128. */
+absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const void* k, const void* v,
+                                 const absa_cluster_lists* lists, void* o, void* stream);
+
+/* ---------------------------------------------------------------------------
  * FP8 (E4M3) variant of the attention step.  The VC-Attention page (section
  * "İki darboğaz") puts most low-bit attention error in the value term, removes
  * part of it by subtracting a per-block mean of V before quantising, and writes

@@ -50,10 +50,11 @@ def test_struct_layouts_match_header():
 #include <stddef.h>
 #include "absa.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(absa_problem), offsetof(absa_problem, scale),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(absa_problem), offsetof(absa_problem, scale),
          offsetof(absa_problem, out_bf16), sizeof(absa_select_params),
          offsetof(absa_select_params, seed), offsetof(absa_select_params, mode), sizeof(absa_blocklist),
-         sizeof(absa_fp8_operands), offsetof(absa_fp8_operands, qk_int8));
+         sizeof(absa_fp8_operands), offsetof(absa_fp8_operands, qk_int8), sizeof(absa_cluster_lists),
+         offsetof(absa_cluster_lists, clusters));
   return 0;
 }
 '''
@@ -67,7 +68,8 @@ int main(void) {
     P, SP, BL = _lib.AbsaProblem, _lib.AbsaSelectParams, _lib.AbsaBlockList
     F8 = _lib.AbsaFp8Operands
     assert vals == [ctypes.sizeof(P), P.scale.offset, P.out_bf16.offset, ctypes.sizeof(SP), SP.seed.offset,
-                    SP.mode.offset, ctypes.sizeof(BL), ctypes.sizeof(F8), F8.qk_int8.offset]
+                    SP.mode.offset, ctypes.sizeof(BL), ctypes.sizeof(F8), F8.qk_int8.offset,
+                    ctypes.sizeof(_lib.AbsaClusterLists), _lib.AbsaClusterLists.clusters.offset]
 
 
 def prob(**kw):
@@ -198,6 +200,35 @@ def test_fp8_validation(lib):
     assert a(P, O, None, FAKE + 8, None) == _lib.ABSA_ERR_ALIGNMENT
     assert a(P, O, ctypes.byref(lists(cap=0)), FAKE, None) == _lib.ABSA_ERR_SHAPE
     assert a(P, ctypes.byref(fp8_ops(q8=None)), None, FAKE, None) == _lib.ABSA_ERR_INVALID_ARG
+
+
+def cl_lists(**kw):
+    base = dict(count=FAKE, kv_idx=FAKE, w=FAKE, label=FAKE, cap=64, clusters=4)
+    base.update(kw)
+    return _lib.AbsaClusterLists(**base)
+
+
+def test_cluster_validation(lib):
+    P = ctypes.byref(prob())
+    S = ctypes.byref(params())
+    n, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.absa_select_clusters_workspace(P, S, ctypes.byref(n)) == 0
+    assert lib.absa_select_workspace(P, S, ctypes.byref(n1)) == 0 and n.value > n1.value
+    ws = n.value
+    sel = lib.absa_select_clusters
+    assert sel(P, S, FAKE, FAKE, ctypes.byref(cl_lists()), FAKE, ws - 1, None) == _lib.ABSA_ERR_WORKSPACE
+    assert sel(P, S, FAKE, FAKE, ctypes.byref(cl_lists(cap=63)), FAKE, ws, None) == _lib.ABSA_ERR_SHAPE
+    assert sel(P, S, FAKE, FAKE, ctypes.byref(cl_lists(clusters=2)), FAKE, ws, None) == _lib.ABSA_ERR_SHAPE
+    assert sel(P, S, FAKE, FAKE, ctypes.byref(cl_lists(label=None)), FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert sel(P, S, FAKE, FAKE, ctypes.byref(cl_lists(w=FAKE + 2)), FAKE, ws, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert sel(P, S, None, FAKE, ctypes.byref(cl_lists()), FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    att = lib.absa_attend_clusters
+    P128 = ctypes.byref(prob(q_block=128))
+    assert att(P, FAKE, FAKE, FAKE, ctypes.byref(cl_lists()), FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED  # Bq 64
+    assert att(P128, FAKE, FAKE, FAKE, ctypes.byref(cl_lists(clusters=3)), FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
+    assert att(P128, FAKE, FAKE, FAKE, None, FAKE, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert att(P128, FAKE, FAKE, FAKE, ctypes.byref(cl_lists(cap=10)), FAKE, None) == _lib.ABSA_ERR_SHAPE
+    assert att(P128, FAKE, FAKE, FAKE, ctypes.byref(cl_lists()), None, None) == _lib.ABSA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

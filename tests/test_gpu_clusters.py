@@ -1,0 +1,150 @@
+"""GPU parity of per-cluster lists (absa_select_clusters / absa_attend_clusters) against the oracle
+(C1..C4 in oracle/cluster_oracle.py).
+
+* Selection is bit-exact on the integer workload (labels, union lists, per-cluster weights) in SIP,
+  TOPK and ALL modes, including a block whose queries all collapse into one cluster; with C = 1 it
+  equals the shared selection bit for bit; on Fourier workloads the per-cluster block decisions
+  agree with the oracle on >= 99.9%.
+* Attention: outputs against the oracle fed the GPU's own labels and lists, to the tolerance of the
+  bf16 path (max-abs <= 1e-2, rel-L2 <= 5e-3)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import gen_config, gen_exact, gen_fourier_heads, bf16_round, Workload
+from gpu_helpers import AGREE, assert_close, dev, errors, keep32, problem, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def absa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import block_sparse_attention_34_amd as m
+    m.library()
+    return m
+
+
+def _workload(H, T, Hs, Ws, d, seed, outliers=False):
+    q, k, v = gen_fourier_heads(T, Hs, Ws, d, 4, 0.3, outliers, seed, list(range(H)))
+    L = T * Hs * Ws
+    sh = (1, H, L, d)
+    return Workload(q=bf16_round(q.reshape(sh)), k=bf16_round(k.reshape(sh)), v=bf16_round(v.reshape(sh)),
+                    B=1, H=H, L=L, d=d, T=T, Hs=Hs, Ws=Ws, q_block=128, kv_block=16, keep=0.25)
+
+
+def _host(lists):
+    return (lists.count.cpu().numpy(), lists.kv_idx.cpu().numpy(), lists.w.cpu().numpy(),
+            lists.label.cpu().numpy())
+
+
+def _per_cluster(count, kv, W, r, C):
+    """The clusters' own lists of row r from its union and weights."""
+    c = int(count[r])
+    idx, w = kv[r, :c], W[r, :c]
+    return [(idx[w[:, j] > 0], w[w[:, j] > 0, j], None) for j in range(C)]
+
+
+@pytest.mark.parametrize("seed,collapse", [(0, False), (1, False), (2, True)])
+@pytest.mark.parametrize("mode", [O.SEL_SIP, O.SEL_TOPK, O.SEL_ALL])
+def test_cluster_select_bit_exact_on_integer_inputs(absa, seed, collapse, mode):
+    wl = gen_exact(seed, groups_collapse=collapse)
+    p = problem(wl)
+    lists, _ = absa.select_clusters(p, dev(wl.q), dev(wl.k), 0.25, clusters=4, kmeans_steps=3,
+                                    select_scale_log2=1.0, seed=seed + 5, stream_id=3, mode=mode)
+    count, kv, W, lab = _host(lists)
+    res = O.select_clusters(wl.q, wl.k, 64, 16, 0.25, C=4, Tk=3, alpha=1.0, seed=seed + 5, stream=3, mode=mode)
+    for r_i, r in enumerate(res.rows):
+        n = O.valid_len(r % p.nq, 64, wl.L)
+        np.testing.assert_array_equal(lab[r, :n], res.labels[r_i][:n])
+        blk, Wo = O.union_lists(res.lists[r_i])
+        assert count[r] == blk.shape[0], (r, count[r], blk.shape[0])
+        np.testing.assert_array_equal(kv[r, :count[r]], blk)
+        np.testing.assert_array_equal(W[r, :count[r]].view(np.uint32), Wo.view(np.uint32))
+    if mode == O.SEL_SIP and not collapse:
+        assert 16 < count.mean() < 64          # the union of four samples of ~16 blocks each
+
+
+def test_one_cluster_equals_shared_selection(absa):
+    wl = _workload(2, 4, 16, 20, 64, seed=41)
+    p = problem(wl)
+    q, k = dev(wl.q), dev(wl.k)
+    shared, _, _ = absa.select(p, q, k, 0.2, clusters=1, seed=9, stream_id=1)
+    cl, _ = absa.select_clusters(p, q, k, 0.2, clusters=1, seed=9, stream_id=1)
+    c0, k0, w0 = (t.cpu().numpy() for t in shared)
+    c1, k1, W1, lab = _host(cl)
+    np.testing.assert_array_equal(c0, c1)
+    for r in range(p.rows):
+        np.testing.assert_array_equal(k0[r, :c0[r]], k1[r, :c1[r]])
+        np.testing.assert_array_equal(w0[r, :c0[r]].view(np.uint32), W1[r, :c1[r], 0].view(np.uint32))
+    assert (lab == 0).all()
+
+
+def _check(absa, wl, keep, C, rows=None, tag="", seed=0):
+    import torch
+    p = problem(wl)
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    lists, _ = absa.select_clusters(p, q, k, keep, clusters=C, seed=seed)
+    o = absa.attend_clusters(p, q, k, v, lists)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    count, kv, W, lab = _host(lists)
+    rows = list(range(p.rows)) if rows is None else rows
+    res = O.select_clusters(wl.q, wl.k, 128, 16, keep32(keep), C=C, seed=seed, rows=rows)
+    diff = tot = 0
+    got, ref = [], []
+    for r_i, r in enumerate(rows):
+        bh, i = divmod(r, p.nq)
+        n = O.valid_len(i, 128, wl.L)
+        per = _per_cluster(count, kv, W, r, C)
+        # decisions of every (cluster, block) against the oracle's own selection
+        for j in range(C):
+            g = np.zeros(p.nk, bool)
+            g[per[j][0]] = True
+            oo = np.zeros(p.nk, bool)
+            oo[res.lists[r_i][j][0]] = True
+            diff += int((g ^ oo).sum())
+            tot += p.nk
+        ref.append(O.attend_row_clusters(wl.q, wl.k, wl.v, bh, i, 128, 16, lab[r, :n].astype(np.int64), per,
+                                         p.sigma))
+        got.append(o[0, bh, i * 128: i * 128 + n])
+    agree = 1.0 - diff / tot
+    g, rr = np.concatenate(got), np.concatenate(ref)
+    err = errors(g, rr)
+    _say(f"{tag} rows={len(rows)} agreement={agree:.6f} max_abs={err[0]:.3e} rel_l2={err[1]:.3e} "
+         f"mean_union={count.mean():.1f}")
+    assert agree >= AGREE, f"{tag}: decision agreement {agree}"
+    assert_close(g, rr, tag)
+    for r in rows:
+        c = count[r]
+        assert (np.diff(kv[r, :c]) > 0).all() and (kv[r, :c] < p.nk).all()
+        assert ((W[r, :c] == 0) | (W[r, :c] >= 1)).all() and (W[r, :c].max(axis=1) >= 1).all()
+
+
+@pytest.mark.parametrize("d,C", [(128, 4), (64, 2), (128, 8)])
+def test_cluster_attend_matches_oracle(absa, d, C):
+    wl = _workload(2, 3, 16, 21, d, seed=43)   # L = 1008: ragged query and KV tails
+    _check(absa, wl, 0.25, C, tag=f"clusters d={d} C={C}")
+
+
+def test_cluster_empty_cluster_rows(absa):
+    # a query block whose queries are all equal: one cluster holds every query, the others are empty
+    wl = _workload(1, 2, 16, 16, 128, seed=44)
+    wl.q[0, 0, 128:256] = wl.q[0, 0, 128]
+    _check(absa, wl, 0.3, 4, tag="clusters with empty clusters")
+
+
+def test_cluster_wan14b_720p_sampled(absa):
+    wl = gen_config(3)
+    p = problem(wl)
+    rows = sample_rows(p.nq, wl.H, 24)
+    _check(absa, wl, 0.095, 4, rows=rows, tag="clusters Wan2.1-14B 720p (sampled rows)")
