@@ -125,6 +125,25 @@ def ablation(args):
         run("mean query+top-k (prior art)", 64, 0.10, "topk", 0, clusters=1)
         run("mean query+SIP", 64, 0.10, "sip", 0, clusters=1)
 
+        # per-cluster lists (one SIP sample per IBCS cluster, each query over its own cluster's
+        # list): the same per-cluster budget as the shared 9.5% row, and a smaller one whose
+        # union is about as large as the shared list
+        def run_clusters(label, keep, seed):
+            cl = absa.alloc_cluster_lists(p16, 4)
+            ws = torch.empty(absa.select_clusters_workspace_bytes(p16, keep), dtype=torch.uint8, device="cuda")
+            t_sel = timed(lambda: absa.select_clusters(p16, q, k, keep, seed=seed, lists=cl, workspace=ws))
+            t_att = timed(lambda: absa.attend_clusters(p16, q, k, v, cl, out=o))
+            err = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
+            kept = float(cl.count.double().mean()) / p16.nk
+            rows.append((label, 16, keep, seed, 4, kept, err, t_sel, t_att))
+            print(f"[ablation] temp {temp} {label} keep={keep} seed={seed}: union {kept:.4f} rel-L2 {err:.4e} "
+                  f"select {t_sel:.2f} ms attend {t_att:.2f} ms", file=sys.stderr, flush=True)
+            del ws
+
+        for seed in (0, 1, 2):
+            run_clusters("IBCS+SIP per cluster", 0.095, seed)
+        run_clusters("IBCS+SIP per cluster", 0.035, 0)
+
         # FP8 path (d = 128, Bk = 16): E4M3 or INT8 QK, ExpCast P and block-mean-centred E4M3 V;
         # dense (every key) and with the SIP lists at keep 9.5%, seed 0
         lists = absa.alloc_lists(p16)
@@ -149,8 +168,8 @@ def ablation(args):
         print(f"### {'with' if outliers else 'without'} outlier tokens, queries scaled by {temp}: effective keys per query "
               f"{np.mean(eff):.1f}; dense attention {t_dense:.2f} ms "
               f"({dense_flops / (t_dense * 1e-3) / 1e12:.0f} TFLOP/s)\n")
-        print("| selection | Bk | keep | seed | C | kept fraction | rel-L2 vs dense | select ms | attend ms |"
-              " dense-equiv. TFLOP/s (select+attend) |")
+        print("| selection | Bk | keep | seed | C | kept fraction (per-cluster rows: of the union) | rel-L2 vs dense |"
+              " select ms | attend ms | dense-equiv. TFLOP/s (select+attend) |")
         print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
         for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
             print(f"| {label} | {Bk} | {keep:.3f} | {seed} | {C} | {kept:.4f} | {err:.3e} | {ts:.2f} | {ta:.2f} | "
@@ -165,8 +184,11 @@ def ablation(args):
         for (label, Bk, keep, seed, C, kept, err, ts, ta) in rows:
             if label == "IBCS+SIP" and Bk == 16 and keep in (0.08, 0.095, 0.11):
                 sip.setdefault(keep, []).append(err)
+            if label == "IBCS+SIP per cluster" and keep == 0.095:
+                sip.setdefault("per-cluster 0.095", []).append(err)
         print("\nSIP rel-L2, mean +- sd over seeds 0-2 (Bk 16): " + "; ".join(
-            f"keep {kp:.3f}: {np.mean(e):.3e} +- {np.std(e, ddof=1):.1e}" for kp, e in sip.items()) + "\n", flush=True)
+            f"keep {kp if isinstance(kp, str) else format(kp, '.3f')}: {np.mean(e):.3e} +- {np.std(e, ddof=1):.1e}"
+            for kp, e in sip.items()) + "\n", flush=True)
 
 
 def attend_source_digest():
