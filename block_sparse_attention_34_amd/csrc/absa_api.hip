@@ -70,7 +70,7 @@ absa_status check_params(const absa_problem* p, const absa_select_params* s, Sel
   return ABSA_OK;
 }
 
-constexpr int kWsRegions = 6;  // the first 5 are published by absa_select_workspace_layout
+constexpr int kWsRegions = 7;  // the first 5 are published by absa_select_workspace_layout
 
 struct WsLayout {
   size_t off[kWsRegions];
@@ -89,11 +89,13 @@ WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
   w.off[3] = o;
   o = align_up(o + (size_t)dm.rows * dm.NK * sizeof(float), kWsAlign);
   w.off[4] = o;
-  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
+  o = align_up(o + (size_t)dm.rows * C * dm.NKp * sizeof(float), kWsAlign);
   w.off[5] = o;
   int per;
   const int nsplit = absa::logit_splits(dm.NQ, C, (int)dm.BH, dm.NKp, &per);
   o = align_up(o + (size_t)dm.rows * C * nsplit * 2 * sizeof(float), kWsAlign);
+  w.off[6] = o;
+  o = align_up(o + (size_t)2 * dm.BH * dm.NKp * p->d * sizeof(uint16_t), kWsAlign);
   w.total = o;
   return w;
 }
@@ -268,6 +270,7 @@ static absa::SelectLaunch select_launch(const absa_problem* prob, const absa_sel
   a.s = reinterpret_cast<float*>(ws + w.off[3]);
   a.logit = reinterpret_cast<float*>(ws + w.off[4]);
   a.mz = reinterpret_cast<float2*>(ws + w.off[5]);
+  a.kbh = reinterpret_cast<uint16_t*>(ws + w.off[6]);
   return a;
 }
 

@@ -13,6 +13,7 @@ struct SelectLaunch {
   float nstar, alpha;
   uint32_t key0, key1, ctr3;
   float* kbarT;  // workspace: [BH][d][NKp]
+  uint16_t* kbh; // workspace: [2][BH][NKp][d] bf16 head, then tail, of the block means
   float* mu;     // workspace: [rows][C][d]
   int* nj;       // workspace: [rows][C]
   float* s;      // workspace: [rows][NK]

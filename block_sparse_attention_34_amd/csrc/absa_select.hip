@@ -1,9 +1,11 @@
 // Block selection kernels for gfx950: KV block means, IBCS in-block k-means,
 // IBCS block scoring and SIP sampling (AB-Attention page, section "AB-Attention
 // ve Üç Temel Yeniliği", IBCS and SIP items).  The rules each kernel follows are
-// listed in absa.h.  Everything is fp32 with correctly rounded divisions, so on
-// inputs whose intermediates are exactly representable the lists and
+// listed in absa.h.  Everything is fp32 with correctly rounded divisions (the
+// two contractions use split bf16 operands, exact for operands bf16 holds), so
+// on inputs whose intermediates are exactly representable the lists and
 // probabilities equal those of an exact computation.
+#include "absa_attend_tiles.h"
 #include "absa_device.h"
 #include "absa_launch.h"
 
@@ -19,11 +21,15 @@ namespace absa {
 __device__ __forceinline__ float exp2_split(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================================================================= K1
-// kbar^T[bh][c][b] = (1/n_b) sum_{valid keys of block b} K[bh][key][c].
+// kbar^T[bh][c][b] = (1/n_b) sum_{valid keys of block b} K[bh][key][c], and the
+// same means block-major as bf16 head and tail, hi = bf16(kbar), lo =
+// bf16(kbar - hi) (kbh[bh][b][c], then kbl at kbh + BH NKp D), the operands of
+// the logit product.  Padding blocks (b >= NK) are 0.
 // Grid (NKp/64, BH), 256 threads; a workgroup produces 64 blocks x D dims.
 template <int D>
 __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __restrict__ k,
-                                                            float* __restrict__ kbarT, int L, int Bk,
+                                                            float* __restrict__ kbarT,
+                                                            uint16_t* __restrict__ kbh, int L, int Bk,
                                                             int NK, int NKp) {
   constexpr int CPR = D / 8;            // 16-byte chunks per key row
   constexpr int BPP = 256 / CPR;        // blocks per pass
@@ -74,6 +80,21 @@ __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __re
   for (int idx = t; idx < D * 64; idx += 256) {
     const int cc = idx >> 6, bl = idx & 63;
     dst[(size_t)cc * NKp + bl] = tile[cc][bl];
+  }
+  const size_t tail = (size_t)gridDim.y * NKp * D;
+  for (int idx = t; idx < 64 * D / 8; idx += 256) {
+    const int bl = idx / (D / 8), c8 = idx % (D / 8);
+    bf16x8 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = tile[c8 * 8 + e][bl];
+      const __bf16 hi = (__bf16)x;
+      hv[e] = hi;
+      lv[e] = (__bf16)(x - (float)hi);
+    }
+    const size_t o = ((size_t)bh * NKp + b0 + bl) * D + c8 * 8;
+    *reinterpret_cast<bf16x8*>(kbh + o) = hv;
+    *reinterpret_cast<bf16x8*>(kbh + tail + o) = lv;
   }
 }
 
@@ -262,20 +283,32 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
 
 // ============================================================================= K2b
 // Block logits l[row][j][b] = alpha * (mu_j . kbar_b) for every centroid of a
-// head against every KV block: a [NQ*C x d] x [d x NK] product on fp32 MFMA
-// (v_mfma_f32_32x32x2_f32, fp32 products and sums).  Workgroup = 4 waves x 32
-// centroids; a wave keeps its centroids as A operands in registers and streams
-// 32-block tiles of kbar^T through LDS.  Grid (ceil(M/128), BH, nsplit): split
-// z covers a contiguous range of 32-block tiles.
+// head against every KV block: a [NQ*C x d] x [d x NK] product on the bf16
+// matrix core.  Each fp32 operand x is split into a bf16 head and tail,
+// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) and |r| <= 2^-17 |x|,
+// and mu . kbar is formed as hi.hi' + hi.lo' + lo.hi' in one fp32 accumulator:
+// the dropped lo.lo' and remainder terms are below 2^-15 of each product, and
+// operands that bf16 holds exactly (lo = 0) give the exact fp32 dot product.
+// Workgroup = 4 waves x 32 centroids; a wave keeps its centroids' heads and
+// tails as A operands in registers and streams 32-block tiles of the means'
+// heads and tails (split once, by K1) through LDS.  Logit rows have NKp
+// entries (the padding holds -inf and is never read); a wave turns its 32 x 32
+// logits around in LDS so that each lane stores 16 contiguous bytes.  Grid (ceil(M/128), BH, nsplit): split z
+// covers a contiguous range of 32-block tiles.
 template <int D>
-__global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict__ kbarT,
+__global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restrict__ kbh,
                                                          const float* __restrict__ mu,
                                                          float* __restrict__ logit,
                                                          float2* __restrict__ mz, int M, int NK,
                                                          int NKp, int L, int Bk, int tiles_per_split,
                                                          float alpha) {
-  constexpr int KS = D / 2;  // k-steps of 2 dims
-  __shared__ __attribute__((aligned(16))) float kt[2][D * 32];
+  constexpr int KS = D / 16;  // k-steps of 16 dims
+  constexpr int NP = 2 * D;   // (4-channel, 4-block) groups of a tile
+  // [buffer][block row][D] bf16, 16-byte chunks swizzled by row as in the
+  // attention kernels' K tiles, so the 32 rows a k-step reads are conflict-free
+  __shared__ __attribute__((aligned(16))) unsigned char khi[2][32 * D * 2], klo[2][32 * D * 2];
+  constexpr int LPS = 40;  // row stride of a wave's logit patch (the two half-waves' writes hit disjoint banks)
+  __shared__ __attribute__((aligned(16))) float lpatch[4][32 * LPS];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) index
   const int h = lane >> 5, n = lane & 31;
@@ -286,40 +319,54 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
   const int tile1 = min(ntile_all, tile0 + tiles_per_split);
   if (tile0 >= tile1) return;
 
-  // A operands: lane (h, n) holds mu[m0 + n][2 s + h]
-  float areg[KS];
+  // A operands: lane (h, n) holds mu[m0 + n][16 s + 8 h + e], e = 0..7, as head and tail
+  bf16x8 ahi[KS], alo[KS];
   {
     const int m = m0 + n;
-    const float* src = mu + ((size_t)bh * M + (m < M ? m : 0)) * D;
+    const f32x4* src = reinterpret_cast<const f32x4*>(mu + ((size_t)bh * M + (m < M ? m : 0)) * D);
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) areg[s2] = (m < M) ? src[2 * s2 + h] : 0.f;
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4) {
+        f32x4 x4 = src[4 * s2 + 2 * h + q4];
+        if (m >= M) x4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 hi = (__bf16)x4[e];
+          ahi[s2][4 * q4 + e] = hi;
+          alo[s2][4 * q4 + e] = (__bf16)(x4[e] - (float)hi);
+        }
+      }
   }
-  const float* kb = kbarT + (size_t)bh * D * NKp;
-  typedef float f32v4 __attribute__((ext_vector_type(4)));  // kept in VGPRs
-  f32v4 stage[D / 32];
+  // 16-byte chunks of a tile: NCK per operand (head, tail), NST per thread
+  constexpr int NCK = 32 * D / 8, NST = 2 * NCK / 256;
+  const uint16_t* kb = kbh + (size_t)bh * NKp * D;
+  const size_t tail = (size_t)gridDim.y * NKp * D;
+  u32x4 stage[NST];
   auto fetch = [&](int tile) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int idx = t + 256 * i;  // 16-byte index in the [D][32] tile
-      const int c = idx >> 3, b4 = idx & 7;
-      stage[i] = *reinterpret_cast<const f32v4*>(kb + (size_t)c * NKp + tile * 32 + b4 * 4);
+    for (int i = 0; i < NST; ++i) {
+      const int idx = t + 256 * i, rem = idx % NCK;
+      stage[i] = *reinterpret_cast<const u32x4*>(kb + (idx >= NCK ? tail : 0) + (size_t)(tile * 32) * D + rem * 8);
     }
   };
   auto put = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int idx = t + 256 * i;
-      *reinterpret_cast<f32v4*>(&kt[buf][idx * 4]) = stage[i];
+    for (int i = 0; i < NST; ++i) {
+      const int idx = t + 256 * i, rem = idx % NCK;
+      const int off = k_off<D>(rem / (D / 8), rem % (D / 8));
+      *reinterpret_cast<u32x4*>(idx >= NCK ? &klo[buf][off] : &khi[buf][off]) = stage[i];
     }
   };
   fetch(tile0);
   put(0);
   // this wave's output window: logit rows m0 .. m0+31 (those below M) of the head
   const int rows_here = max(0, min(32, M - m0));
-  const uint64_t obase = (uint64_t)(logit + ((size_t)bh * M + (rows_here > 0 ? m0 : 0)) * NK);
+  const uint64_t obase = (uint64_t)(logit + ((size_t)bh * M + (rows_here > 0 ? m0 : 0)) * NKp);
   const uint32_t obase_lo = __builtin_amdgcn_readfirstlane((uint32_t)obase);
   const uint32_t obase_hi = __builtin_amdgcn_readfirstlane((uint32_t)(obase >> 32));
-  const int obytes = __builtin_amdgcn_readfirstlane(rows_here * NK * 4);
+  const int obytes = __builtin_amdgcn_readfirstlane(rows_here * NKp * 4);
+  float* const lp = lpatch[w];
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(((uint64_t)obase_hi << 32) | obase_lo), 0, obytes, 0x00020000);
   // running max m and normaliser Z = sum nk 2^(l - m) of the 16 centroids this
@@ -332,31 +379,49 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const float* __restrict
     const int buf = (tile - tile0) & 1;
     __syncthreads();
     if (tile + 1 < tile1) fetch(tile + 1);
+    // B operands: lane (h, n) reads block n, channels 16 s + 8 h .. +7
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    // all of the tile's operand reads in flight before the products
+    bf16x8 bhi[KS], blo[KS];
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(areg[s2], kt[buf][(2 * s2 + h) * 32 + n], acc, 0, 0, 0);
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const int off = k_off<D>(n, 2 * s2 + h);
+      bhi[s2] = *reinterpret_cast<const bf16x8*>(&khi[buf][off]);
+      blo[s2] = *reinterpret_cast<const bf16x8*>(&klo[buf][off]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s2], bhi[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s2], blo[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[s2], bhi[s2], acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // the reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 3 * KS, 0);  // then the products
     // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
     // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
-    // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z, and their
-    // stores (like those of rows >= M) fall outside the window and are dropped.
+    // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z; stores
+    // of rows >= M fall outside the window and are dropped.
     const int b = tile * 32 + n;
     const bool bv = b < NK;
     const float nk = (float)min(Bk, L - b * Bk);
-    const int vo = bv ? (4 * h * NK + b) * 4 : 0x7FFFFFF0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float l = bv ? alpha * acc[r] : -INFINITY;
-      const uint32_t lbits = __float_as_uint(l);
-      const int so = (8 * (r >> 2) + (r & 3)) * NK * 4;
-      __builtin_amdgcn_raw_buffer_store_b32(lbits, ors, vo, so, 0);
+      lp[(8 * (r >> 2) + 4 * h + (r & 3)) * LPS + n] = l;
       const float dd = fabsf(rm[r] - l);
       const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
       const bool up = l > rm[r];
       rz[r] = fmaf(rz[r], up ? e : 1.f, up ? nk : nk * e);
       rm[r] = up ? l : rm[r];
+    }
+    // lane i stores blocks 4 (i % 8) .. +3 of patch rows 8 q + i / 8
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pr = 8 * q + (lane >> 3), c4 = 4 * (lane & 7);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&lp[pr * LPS + c4]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ors, (pr * NKp + tile * 32 + c4) * 4, 0, 0);
     }
     if (tile + 1 < tile1) put(buf ^ 1);
   }
@@ -443,7 +508,7 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
                                                      const float2* __restrict__ mz, int nsplit,
                                                      const int* __restrict__ nj,
                                                      float* __restrict__ s_out, int L, int Bq, int Bk,
-                                                     int NK, int NQ,
+                                                     int NK, int NKp, int NQ,
                                                      float nstar, int kstar, int mode, uint32_t key0,
                                                      uint32_t key1, uint32_t ctr3,
                                                      int32_t* __restrict__ count_out,
@@ -472,7 +537,7 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
   // max dropped; combined from the logit kernel's per-split partials), then
   // s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j.
   {
-    const float* lrow = logit + (size_t)row * C * NK;
+    const float* lrow = logit + (size_t)row * C * NKp;
     __shared__ float coef_s[C], mj_s[C];
     if (t < C) {
       const float2* pz = mz + ((size_t)row * C + t) * nsplit;
@@ -505,7 +570,7 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
 #pragma unroll
         for (int j = 0; j < C; ++j) {
           const int b = b0 + u * SIP_NT;
-          lv[u][j] = (b < NK) ? lrow[(size_t)j * NK + b] : -INFINITY;
+          lv[u][j] = (b < NK) ? lrow[(size_t)j * NKp + b] : -INFINITY;
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -681,9 +746,9 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   {
     dim3 grid(a.NKp / 64, BH);
     if (a.d == 128)
-      kv_block_mean_kernel<128><<<grid, 256, 0, st>>>(a.k, a.kbarT, a.L, a.Bk, a.NK, a.NKp);
+      kv_block_mean_kernel<128><<<grid, 256, 0, st>>>(a.k, a.kbarT, a.kbh, a.L, a.Bk, a.NK, a.NKp);
     else
-      kv_block_mean_kernel<64><<<grid, 256, 0, st>>>(a.k, a.kbarT, a.L, a.Bk, a.NK, a.NKp);
+      kv_block_mean_kernel<64><<<grid, 256, 0, st>>>(a.k, a.kbarT, a.kbh, a.L, a.Bk, a.NK, a.NKp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -718,10 +783,10 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
     dim3 grid(mtiles, BH, nsplit);
     if (a.d == 128)
-      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
+      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbh, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
                                                    a.Bk, per, a.alpha);
     else
-      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbarT, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
+      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbh, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
                                                   a.Bk, per, a.alpha);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -734,7 +799,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     const dim3 sgrid(rows, a.per_cluster ? a.C : 1);
 #define ABSA_SIP(CC)                                                                                   \
   sip_kernel<CC><<<sgrid, SIP_NT, lds, st>>>(a.logit, a.mz, nsplit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK,  \
-                                             a.NQ, a.nstar,                                              \
+                                             a.NKp, a.NQ, a.nstar,                                              \
                                              a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
                                              a.inv_pi, a.cap, a.pi_out, a.per_cluster)
     switch (a.C) {

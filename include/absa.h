@@ -22,7 +22,10 @@
  *                      empty clusters keep their centroid;
  *   score s_b          sum_j (n_j/n) * nk_b * 2^(l_jb - m_j) / Z_j with
  *                      l_jb = alpha * mu_j . kbar_b, m_j = max_b l_jb, terms
- *                      with l_jb - m_j < -64 dropped, Z_j normalising;
+ *                      with l_jb - m_j < -64 dropped, Z_j normalising; the dot
+ *                      products split each fp32 operand into a bf16 head and
+ *                      tail (hi.hi' + hi.lo' + lo.hi', fp32 sums): exact when
+ *                      bf16 holds mu and kbar, ~2^-15 relative otherwise;
  *   inclusion pi_b     min(1, lambda s_b) with sum_b pi_b = keep * NK,
  *                      solved by iterative capping, rounded to fp32;
  *   draw               Philox4x32-10 (Salmon et al., SC'11) with counter
@@ -133,7 +136,7 @@ absa_status absa_select_workspace(const absa_problem* prob, const absa_select_pa
  *   offsets[1]  mu      fp32 [rows][C][d]   final centroids
  *   offsets[2]  n_j     int32 [rows][C]     final cluster sizes
  *   offsets[3]  s       fp32 [rows][NK]     block scores
- *   offsets[4]  l       fp32 [rows][C][NK]  block logits alpha * mu_j . kbar_b
+ *   offsets[4]  l       fp32 [rows][C][NKp] block logits alpha * mu_j . kbar_b
  * ([host] pointers; offsets has 5 entries). */
 absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
                                          size_t* offsets);

@@ -117,8 +117,9 @@ def test_workspace_size_and_layout(lib):
     # kbar^T [2][64][64] f32, mu [32][4][64] f32, n_j [32][4] i32, s [32][64] f32,
     # logits [32][4][64] f32, each 256-aligned
     assert list(offs) == [0, 32768, 32768 + 32768, 65536 + 512, 65536 + 512 + 8192]
-    # + per-split (max, normaliser) of each centroid: 2 splits of the 64 blocks here
-    assert n.value == 65536 + 512 + 8192 + 32 * 4 * 64 * 4 + 32 * 4 * 2 * 8
+    # + per-split (max, normaliser) of each centroid: 2 splits of the 64 blocks here,
+    # + the block means' bf16 heads and tails [2][2][64][64]
+    assert n.value == 65536 + 512 + 8192 + 32 * 4 * 64 * 4 + 32 * 4 * 2 * 8 + 2 * 2 * 64 * 64 * 2
     for bad, code in ((dict(keep=0.0), -1), (dict(keep=1.5), -1), (dict(keep=float("nan")), -1),
                       (dict(clusters=3), -3), (dict(clusters=-1), -1), (dict(kmeans_steps=65), -1),
                       (dict(mode=7), -1), (dict(select_scale_log2=float("inf")), -1)):
