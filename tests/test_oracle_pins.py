@@ -12,7 +12,8 @@ import scipy.special
 import torch
 
 import oracle as O
-from workloads import gen_config, gen_exact, gen_micro
+from golden_figures import page_figure
+from workloads import CONFIGS, gen_config, gen_exact, gen_micro
 
 
 # ----------------------------------------------------------------------------- dense ([XA] formula)
@@ -424,3 +425,13 @@ def test_cluster_estimator_all_blocks_is_dense_and_members_use_their_list():
     got = O.attend_row_clusters(wl.q, wl.k, wl.v, 0, 0, wl.q_block, wl.kv_block, lab, lists, sigma)
     num, den = O.estimator_num_den(wl.q[0, 0, [3]], wl.k[0, 0], wl.v[0, 0], [2], [4.0], wl.kv_block, sigma)
     np.testing.assert_allclose(got[3], (num / den[:, None])[0], rtol=1e-12)
+
+
+def test_page_scale_budgets_sit_in_the_reported_skip_range():
+    # The AB-Attention page reports 89-92% of the attention work skipped on Wan2.1 and
+    # HunyuanVideo; the page-scale workloads keep the complementary 8-11% of the KV blocks.
+    lo = 1.0 - page_figure("skipped_fraction_max")
+    hi = 1.0 - page_figure("skipped_fraction_min")
+    for cfg in (2, 3, 4):
+        for keep in CONFIGS[cfg].keep:
+            assert lo - 1e-9 <= keep <= hi + 1e-9, (cfg, keep)
