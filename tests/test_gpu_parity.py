@@ -179,6 +179,26 @@ def test_tiny_workload_end_to_end(absa):
     _check_selection_and_attend(absa, wl, 0.25, tag="tiny")
 
 
+@pytest.mark.parametrize("T,Hs,Ws,Bq,keep", [
+    (1, 1, 1, 64, 0.5),     # L = 1: one query, one KV block of one key
+    (1, 1, 17, 64, 0.5),    # L = 17: a second KV block of one key
+    (1, 5, 26, 128, 0.3),   # L = 130: a second query block of two queries
+])
+def test_degenerate_lengths(absa, T, Hs, Ws, Bq, keep):
+    wl = _random_workload(2, T, Hs, Ws, 64, Bq, 16, seed=T * 1000 + Hs * 37 + Ws, keep=keep)
+    for seed in range(4):  # several draws: kept and dropped blocks, empty lists
+        _check_selection_and_attend(absa, wl, keep, seed=seed, tag=f"L={wl.L} seed {seed}")
+
+
+def test_maximum_kv_blocks(absa):
+    # NK = 12288, the most the selection accepts (48 blocks per thread of the SIP kernel)
+    wl = _random_workload(2, 48, 64, 64, 128, 128, 16, seed=47, keep=0.08)
+    p = problem(wl)
+    assert p.nk == 12288
+    rows = sample_rows(p.nq, wl.H, 16)
+    _check_selection_and_attend(absa, wl, 0.08, rows=rows, tag="NK = 12288 (sampled rows)")
+
+
 @pytest.mark.parametrize("d,Bq,Bk", [(128, 128, 16), (128, 64, 32), (64, 128, 64), (128, 128, 32),
                                      (128, 128, 64), (64, 64, 16)])
 def test_block_size_variants(absa, d, Bq, Bk):
