@@ -293,8 +293,9 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
 // tails as A operands in registers and streams 32-block tiles of the means'
 // heads and tails (split once, by K1) through LDS.  Logit rows have NKp
 // entries (the padding holds -inf and is never read); a wave turns its 32 x 32
-// logits around in LDS so that each lane stores 16 contiguous bytes.  Grid (ceil(M/128), BH, nsplit): split z
-// covers a contiguous range of 32-block tiles.
+// logits around in LDS so that each lane stores 16 contiguous bytes.
+// Grid (ceil(M/128), BH, nsplit): split z covers a contiguous range of 32-block
+// tiles.
 template <int D>
 __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restrict__ kbh,
                                                          const float* __restrict__ mu,
@@ -303,7 +304,6 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
                                                          int NKp, int L, int Bk, int tiles_per_split,
                                                          float alpha) {
   constexpr int KS = D / 16;  // k-steps of 16 dims
-  constexpr int NP = 2 * D;   // (4-channel, 4-block) groups of a tile
   // [buffer][block row][D] bf16, 16-byte chunks swizzled by row as in the
   // attention kernels' K tiles, so the 32 rows a k-step reads are conflict-free
   __shared__ __attribute__((aligned(16))) unsigned char khi[2][32 * D * 2], klo[2][32 * D * 2];
