@@ -148,3 +148,13 @@ def test_cluster_wan14b_720p_sampled(absa):
     p = problem(wl)
     rows = sample_rows(p.nq, wl.H, 24)
     _check(absa, wl, 0.095, 4, rows=rows, tag="clusters Wan2.1-14B 720p (sampled rows)")
+
+
+def test_cluster_maximum_kv_blocks(absa):
+    # NK = 12288, the most the selection accepts: the per-cluster SIP groups hold 48 blocks per
+    # thread and the union kernel one LDS word per block
+    wl = _workload(1, 48, 64, 64, 128, seed=48)
+    p = problem(wl)
+    assert p.nk == 12288
+    rows = sample_rows(p.nq, wl.H, 8)
+    _check(absa, wl, 0.05, 4, rows=rows, tag="clusters NK = 12288 (sampled rows)")
