@@ -242,6 +242,26 @@ def test_fp8_with_sip_lists_wan14b_720p(absa, qk_int8):
              f"fp8 Wan14B 720p sampled rows ({len(rows)}) int8 QK {qk_int8}", qk_int8)
 
 
+def test_fp8_maximum_kv_blocks(absa):
+    """NK = 12288 (L = 196 608), the largest KV block count: quantisation bit-exact, attention on
+    sampled rows with the library's SIP lists against the oracle."""
+    wl = _workload(1, 48, 64, 64, seed=49, outliers=True)
+    p = problem(wl)
+    assert p.nk == 12288
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    ops, _ = absa.quantize_fp8(p, q, k, v)
+    hds = _check_quantisation(ops, wl, [0])
+    lists, _, _ = absa.select(p, q, k, 0.05, seed=3)
+    o = absa.attend_fp8(p, ops, lists).cpu().numpy()
+    count, kv_idx, inv_pi = lists_to_host(lists)
+    rng = np.random.default_rng(78)
+    rows = sorted(set(int(i) for i in rng.choice(p.nq, 8, replace=False)) | {0, p.nq - 1})
+    ref = _oracle_rows(hds, wl, rows, count, kv_idx, inv_pi, p.nq)
+    got = _gpu_rows(o, wl, rows, p.nq)
+    _compare(np.concatenate([got[r] for r in rows]), np.concatenate([ref[r] for r in rows]),
+             f"fp8 NK = 12288 sampled rows ({len(rows)})")
+
+
 _WAN14 = {}
 
 
