@@ -100,13 +100,13 @@ def ablation(args):
             eff.append(float(torch.exp(-(pr * torch.log(pr + 1e-30)).sum(1)).mean()))
         rows = []
 
-        def run(label, Bk, keep, mode, seed, clusters=4):
+        def run(label, Bk, keep, mode, seed, clusters=4, steps=0):
             p = absa.Problem(wl.B, wl.H, wl.L, wl.d, wl.T, wl.Hs, wl.Ws, wl.q_block, Bk)
             lists = absa.alloc_lists(p)
-            ws = torch.empty(absa.select_workspace_bytes(p, keep, clusters=clusters, mode=mode),
+            ws = torch.empty(absa.select_workspace_bytes(p, keep, clusters=clusters, kmeans_steps=steps, mode=mode),
                              dtype=torch.uint8, device="cuda")
-            sel = lambda: absa.select(p, q, k, keep, clusters=clusters, seed=seed, mode=mode,  # noqa: E731
-                                      lists=lists, workspace=ws)
+            sel = lambda: absa.select(p, q, k, keep, clusters=clusters, kmeans_steps=steps,  # noqa: E731
+                                      seed=seed, mode=mode, lists=lists, workspace=ws)
             t_sel = timed(sel)
             t_att = timed(lambda: absa.attend(p, q, k, v, lists, out=o))
             err = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
@@ -124,6 +124,13 @@ def ablation(args):
             run("IBCS+top-k", Bk, 0.10, "topk", 0)
         run("mean query+top-k (prior art)", 64, 0.10, "topk", 0, clusters=1)
         run("mean query+SIP", 64, 0.10, "sip", 0, clusters=1)
+        # the IBCS knobs at Bk 16, keep 9.5%: cluster count (C = 4 is above) and k-means steps
+        for C in (1, 2, 8):
+            run("IBCS+SIP, C sweep", 16, 0.095, "sip", 0, clusters=C)
+            run("IBCS+top-k, C sweep", 16, 0.095, "topk", 0, clusters=C)
+        for steps in (1, 2):
+            run(f"IBCS+SIP, {steps} k-means step{'s' if steps > 1 else ''}", 16, 0.095, "sip", 0, steps=steps)
+            run(f"IBCS+top-k, {steps} k-means step{'s' if steps > 1 else ''}", 16, 0.095, "topk", 0, steps=steps)
 
         # per-cluster lists (one SIP sample per IBCS cluster, each query over its own cluster's
         # list): the same per-cluster budget as the shared 9.5% row, and a smaller one whose
