@@ -158,3 +158,19 @@ def test_cluster_maximum_kv_blocks(absa):
     assert p.nk == 12288
     rows = sample_rows(p.nq, wl.H, 8)
     _check(absa, wl, 0.05, 4, rows=rows, tag="clusters NK = 12288 (sampled rows)")
+
+
+def test_cluster_deterministic(absa):
+    # two runs give the same labels, union lists, per-cluster weights and outputs, bit for bit
+    import torch
+    wl = _workload(2, 3, 16, 21, 128, seed=45)
+    p = problem(wl)
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    outs = []
+    for _ in range(2):
+        lists, _ = absa.select_clusters(p, q, k, 0.2, clusters=4, seed=6)
+        o = absa.attend_clusters(p, q, k, v, lists)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (lists.count, lists.kv_idx, lists.w, lists.label, o)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -262,6 +262,24 @@ def test_fp8_maximum_kv_blocks(absa):
              f"fp8 NK = 12288 sampled rows ({len(rows)})")
 
 
+@pytest.mark.parametrize("qk_int8", [False, True])
+def test_fp8_deterministic(absa, qk_int8):
+    """Two runs of quantisation and attention give the same bytes (no order-dependent sums)."""
+    import torch
+    wl = _workload(2, 5, 15, 16, seed=31, outliers=True)
+    p = problem(wl)
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    lists, _, _ = absa.select(p, q, k, 0.2, seed=4)
+    outs = []
+    for _ in range(2):
+        ops, _ = absa.quantize_fp8(p, q, k, v, qk_int8=qk_int8)
+        o = absa.attend_fp8(p, ops, lists)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (ops.q8, ops.sq, ops.k8, ops.sk, ops.kbar, ops.v8t, ops.sv, ops.mu, o)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 _WAN14 = {}
 
 
