@@ -260,6 +260,51 @@ def test_sip_average_approaches_dense(absa):
     assert mean_err < 0.5 * np.mean(errs)
 
 
+
+def test_graph_capture_replays_match_eager(absa):
+    # The library allocates nothing, sets no memory and never synchronises, so a step of selection
+    # and attention can be captured into a graph; every replay, with eager work clobbering the
+    # outputs in between, must reproduce the eager result bit for bit.
+    import torch
+    wl = _random_workload(2, 5, 15, 16, 128, 128, 16, seed=11, modes=8)
+    p = problem(wl)
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    lists = absa.alloc_lists(p)
+    ws = torch.empty(absa.select_workspace_bytes(p, 0.1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((p.B, p.H, p.L, p.d), dtype=torch.float32, device="cuda")
+
+    def step():
+        absa.select(p, q, k, 0.1, seed=5, lists=lists, workspace=ws)
+        absa.attend(p, q, k, v, lists, out=o)
+
+    def clobber():
+        o.zero_()
+        lists.count.zero_()
+        lists.kv_idx.zero_()
+        lists.inv_pi.zero_()
+
+    clobber()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (lists.count, lists.kv_idx, lists.inv_pi, o)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        clobber()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((lists.count, lists.kv_idx, lists.inv_pi, o), ref):
+            assert torch.equal(a, b), f"replay {i}"
+
 # ----------------------------------------------------------------------------- full-size workloads
 
 def test_wan13b_480p_full(absa):
