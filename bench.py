@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1920)
-    ap.add_argument("--extra", action="store_true", help="also time the dense kernel")
+    ap.add_argument("--extra", action="store_true", help="also time the dense kernel, the FP8 variant and per-cluster lists")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the JSON line: accuracy and time of SIP / top-k / block-size / prior-art "
                          "selection against dense attention, as a markdown table")
@@ -392,6 +392,26 @@ def main():
                 line[f"fp8_{tag}_attend_ms"] = e0.elapsed_time(e1) / 5
                 line[f"fp8_{tag}_quantize_ms"] = tq
                 del ops, qws, o8
+            # per-cluster lists (C = 4, the same keep per cluster): selection and attention
+            cl = absa.alloc_cluster_lists(p, 4)
+            cws = torch.empty(absa.select_clusters_workspace_bytes(p, args.keep), dtype=torch.uint8, device="cuda")
+            oc = torch.empty_like(o)
+            absa.select_clusters(p, q, k, args.keep, seed=0, lists=cl, workspace=cws)
+            absa.attend_clusters(p, q, k, v, cl, out=oc)
+            e0.record(stream)
+            for _ in range(3):
+                absa.select_clusters(p, q, k, args.keep, seed=0, lists=cl, workspace=cws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            line["clusters_select_ms"] = e0.elapsed_time(e1) / 3
+            e0.record(stream)
+            for _ in range(3):
+                absa.attend_clusters(p, q, k, v, cl, out=oc)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            line["clusters_attend_ms"] = e0.elapsed_time(e1) / 3
+            line["clusters_union_fraction"] = float(cl.count.double().mean()) / p.nk
+            del cl, cws, oc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.keep, args.kv_block, args.cpu_sample_rows)
     print(json.dumps(line), flush=True)
