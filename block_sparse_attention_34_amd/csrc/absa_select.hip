@@ -570,7 +570,9 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
 #pragma unroll
         for (int j = 0; j < C; ++j) {
           const int b = b0 + u * SIP_NT;
-          lv[u][j] = (b < NK) ? lrow[(size_t)j * NKp + b] : -INFINITY;
+          // (a centroid with coefficient 0 -- an empty cluster, or another
+          // cluster's in a per-cluster sample -- is not read at all)
+          lv[u][j] = (b < NK && coef[j] != 0.f) ? lrow[(size_t)j * NKp + b] : -INFINITY;
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -686,7 +688,8 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
 // One workgroup per row: the ascending union of the row's C cluster lists and
 // the weight of every (entry, cluster) pair, 0 where the cluster did not draw
 // the block.  LDS holds one word per KV block: the cluster mask in the low 8
-// bits, the union position above it.
+// bits, the union position above it.  The weight rows are zeroed with
+// contiguous stores, then each cluster's drawn weights are scattered in.
 __global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __restrict__ ccount,
                                                                const int32_t* __restrict__ cidx,
                                                                const float* __restrict__ cw, int ccap, int C,
@@ -719,12 +722,13 @@ __global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __
     const uint32_t m = slot[b];
     if (m) {
       uidx[row * ucap + pos] = b;
-      for (int j = 0; j < C; ++j)
-        if (!((m >> j) & 1u)) wrow[(size_t)pos * C + j] = 0.f;  // the drawn ones are written below
       slot[b] = ((uint32_t)pos << 8) | m;
       ++pos;
     }
   }
+  // every weight of the union starts at 0 (coalesced); the drawn ones follow
+  // after the barrier, which also orders these stores before them
+  for (int i = t; i < total * C; i += SIP_NT) wrow[i] = 0.f;
   __syncthreads();
   for (int j = 0; j < C; ++j) {
     const int n = min(ccount[row * C + j], ccap);
