@@ -342,15 +342,17 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
   constexpr int NCK = 32 * D / 8, NST = 2 * NCK / 256;
   const uint16_t* kb = kbh + (size_t)bh * NKp * D;
   const size_t tail = (size_t)gridDim.y * NKp * D;
-  u32x4 stage[NST];
-  auto fetch = [&](int tile) {
+  // two register stages: the global loads of a tile are issued two tiles
+  // ahead of its store into LDS, so their latency spans two tile periods
+  u32x4 stA[NST], stB[NST];
+  auto fetch = [&](u32x4 (&stage)[NST], int tile) {
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int idx = t + 256 * i, rem = idx % NCK;
       stage[i] = *reinterpret_cast<const u32x4*>(kb + (idx >= NCK ? tail : 0) + (size_t)(tile * 32) * D + rem * 8);
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&](const u32x4 (&stage)[NST], int buf) {
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int idx = t + 256 * i, rem = idx % NCK;
@@ -358,8 +360,9 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
       *reinterpret_cast<u32x4*>(idx >= NCK ? &klo[buf][off] : &khi[buf][off]) = stage[i];
     }
   };
-  fetch(tile0);
-  put(0);
+  fetch(stA, tile0);
+  put(stA, 0);
+  if (tile0 + 1 < tile1) fetch(stA, tile0 + 1);
   // this wave's output window: logit rows m0 .. m0+31 (those below M) of the head
   const int rows_here = max(0, min(32, M - m0));
   const uint64_t obase = (uint64_t)(logit + ((size_t)bh * M + (rows_here > 0 ? m0 : 0)) * NKp);
@@ -374,16 +377,17 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
   float rm[16], rz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) { rm[r] = -INFINITY; rz[r] = 0.f; }
-#pragma unroll 1
-  for (int tile = tile0; tile < tile1; ++tile) {
+  // one tile: sput holds tile + 1 (stored into the other LDS buffer at the
+  // end), sfetch receives tile + 2; the loop alternates the two stages
+  auto body = [&](int tile, const u32x4 (&sput)[NST], u32x4 (&sfetch)[NST]) {
     const int buf = (tile - tile0) & 1;
     __syncthreads();
-    if (tile + 1 < tile1) fetch(tile + 1);
+    if (tile + 2 < tile1) fetch(sfetch, tile + 2);
     // B operands: lane (h, n) reads block n, channels 16 s + 8 h .. +7
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    // all of the tile's operand reads in flight before the products
+    // operand reads two k-steps ahead of their products (fewer live registers)
     bf16x8 bhi[KS], blo[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
@@ -397,8 +401,12 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s2], blo[s2], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[s2], bhi[s2], acc, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // the reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, 3 * KS, 0);  // then the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      if (s2 + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
     // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
     // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
     // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z; stores
@@ -423,7 +431,12 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
       const u32x4 v = *reinterpret_cast<const u32x4*>(&lp[pr * LPS + c4]);
       __builtin_amdgcn_raw_buffer_store_b128(v, ors, (pr * NKp + tile * 32 + c4) * 4, 0, 0);
     }
-    if (tile + 1 < tile1) put(buf ^ 1);
+    if (tile + 1 < tile1) put(sput, buf ^ 1);
+  };
+#pragma unroll 1
+  for (int tile = tile0; tile < tile1; tile += 2) {
+    body(tile, stA, stB);
+    if (tile + 1 < tile1) body(tile + 1, stB, stA);
   }
   // combine over the 32 blocks (lanes) of each half-wave and write this split's
   // partial (m, Z) of every centroid
