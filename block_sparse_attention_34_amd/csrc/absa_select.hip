@@ -573,7 +573,7 @@ __global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ l
     float mj[C], coef[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) { mj[j] = mj_s[j]; coef[j] = coef_s[j]; }
-    constexpr int U = 4;  // blocks per batch: U*C loads in flight
+    constexpr int U = 8;  // blocks per batch: U*C loads in flight
     float* srow_out = s_out + (size_t)orow * NK;
 #pragma unroll 1
     for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
