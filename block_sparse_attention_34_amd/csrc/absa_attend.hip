@@ -38,10 +38,11 @@ namespace absa {
 // which chunk each lane fetches.  The loop is unrolled by two so every ring
 // slot is a distinct static LDS array.
 
-// Two workgroups of 256 threads per CU (at most 256 VGPRs per lane) hide the
-// barrier of one behind the matrix work of the other.
+// Two workgroups per CU hide the barrier of one behind the matrix work of the
+// other; the second bound is the minimum number of waves per SIMD that allows
+// them (two workgroups of BQ/32 waves over 4 SIMDs).
 template <int D, int BQ, int BK, bool DENSE, bool OUT_BF16>
-__global__ __launch_bounds__(BQ * 2, 512 / (BQ * 2)) void attend_kernel(AttendLaunch a) {
+__global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a) {
   constexpr int NT = BQ * 2;           // threads
   constexpr int NW = BQ / 32;          // waves, 32 queries each
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
