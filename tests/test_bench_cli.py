@@ -1,5 +1,6 @@
-"""CPU check of bench.py's command line: more than one GPU is refused with a message and a non-zero
-status before anything touches a device."""
+"""CPU checks of bench.py's host logic: more than one GPU is refused with a message and a non-zero
+status before anything touches a device, and the attention kernel's HBM traffic is reported only while
+the kernel sources are the ones the committed counter summary was taken on."""
 import os
 import subprocess
 import sys
@@ -12,3 +13,26 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU only" in (r.stdout + r.stderr)
+
+
+def test_traffic_is_reported_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    digest = bench.attend_source_digest()
+    assert len(digest) == 16
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    src = tmp_path / "block_sparse_attention_34_amd" / "csrc"
+    src.mkdir(parents=True)
+    for name in ("absa_attend_tiles.h", "absa_attend.hip", "absa_attend_pp.hip"):
+        (src / name).write_bytes(open(os.path.join(ROOT, "block_sparse_attention_34_amd", "csrc", name), "rb").read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    f = prof / "attend_kernel_t_traffic.md"
+    f.write_text(f"traffic_bytes_per_launch: 123\nattend_source_sha256_16: {digest}\n")
+    assert bench.measured_traffic("t") == 123
+    f.write_text("traffic_bytes_per_launch: 123\nattend_source_sha256_16: 0000000000000000\n")
+    assert bench.measured_traffic("t") is None           # the kernel changed since the counters were taken
+    (src / "absa_attend_pp.hip").write_bytes(b"// edited\n")
+    f.write_text(f"traffic_bytes_per_launch: 123\nattend_source_sha256_16: {digest}\n")
+    assert bench.measured_traffic("t") is None
+    assert bench.measured_traffic("missing") is None
