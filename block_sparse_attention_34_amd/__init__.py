@@ -93,6 +93,39 @@ def _check_qkv(prob: Problem, *ts):
                              f"got {tuple(t.shape)}")
 
 
+def _check_out(prob: Problem, out, device):
+    """A caller-supplied output: [B,H,L,d], contiguous, on the inputs' GPU, bf16 if out_bf16 else fp32."""
+    import torch
+    want = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != device:
+        raise ValueError("out must be a tensor on the same GPU as Q, K, V")
+    if out.dtype != want:
+        raise ValueError(f"out must be {want} (out_bf16={bool(prob.out_bf16)}), got {out.dtype}")
+    if not out.is_contiguous() or tuple(out.shape) != (prob.B, prob.H, prob.L, prob.d):
+        raise ValueError(f"out must be contiguous [B,H,L,d] = {(prob.B, prob.H, prob.L, prob.d)}, "
+                         f"got {tuple(out.shape)}")
+
+
+def _check_lists(prob: Problem, lists, device, need_cap_nk: bool):
+    """Block lists: int32 count [rows], int32 kv_idx and fp32 inv_pi [rows, cap], contiguous, on the
+    inputs' GPU; cap >= 1 (>= NK when the lists are written by a selection)."""
+    import torch
+    count, kv_idx, inv_pi = lists
+    for t, dt, name in ((count, torch.int32, "count"), (kv_idx, torch.int32, "kv_idx"),
+                        (inv_pi, torch.float32, "inv_pi")):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_cuda or t.device != device:
+            raise ValueError(f"lists.{name} must be a {dt} tensor on the same GPU as Q and K")
+        if not t.is_contiguous():
+            raise ValueError(f"lists.{name} must be contiguous")
+    if tuple(count.shape) != (prob.rows,):
+        raise ValueError(f"lists.count must have shape [rows] = [{prob.rows}], got {tuple(count.shape)}")
+    if kv_idx.dim() != 2 or kv_idx.shape[0] != prob.rows or kv_idx.shape != inv_pi.shape:
+        raise ValueError(f"lists.kv_idx and lists.inv_pi must both be [rows, cap] with rows = {prob.rows}")
+    cap = kv_idx.shape[1]
+    if cap < 1 or (need_cap_nk and cap < prob.nk):
+        raise ValueError(f"lists capacity {cap} is too small (needs >= {prob.nk if need_cap_nk else 1})")
+
+
 def num_blocks(prob: Problem) -> Tuple[int, int]:
     nq, nk = ctypes.c_int32(), ctypes.c_int32()
     p = prob.c()
@@ -138,6 +171,7 @@ def select(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmeans_steps:
     import torch
     _check_qkv(prob, q, k)
     lists = alloc_lists(prob, q.device) if lists is None else lists
+    _check_lists(prob, lists, q.device, need_cap_nk=True)
     pi = torch.empty((prob.rows, prob.nk), dtype=torch.float32, device=q.device) if want_pi else None
     nbytes = select_workspace_bytes(prob, keep, clusters, kmeans_steps, select_scale_log2, seed,
                                     stream_id, mode)
@@ -157,9 +191,12 @@ def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):
     """Block-sparse attention over ``lists`` with 1/pi weights.  Returns O [B,H,L,d]."""
     import torch
     _check_qkv(prob, q, k, v)
+    _check_lists(prob, lists, q.device, need_cap_nk=False)
     odt = torch.bfloat16 if prob.out_bf16 else torch.float32
     if out is None:
         out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    else:
+        _check_out(prob, out, q.device)
     p = prob.c()
     bl = lists.c()
     st = library().absa_attend(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
@@ -175,6 +212,8 @@ def dense(prob: Problem, q, k, v, out=None):
     odt = torch.bfloat16 if prob.out_bf16 else torch.float32
     if out is None:
         out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    else:
+        _check_out(prob, out, q.device)
     p = prob.c()
     st = library().absa_dense(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               _stream())
@@ -243,6 +282,10 @@ def attend_fp8(prob: Problem, ops: Fp8Operands, lists: Optional[BlockLists], out
     odt = torch.bfloat16 if prob.out_bf16 else torch.float32
     if out is None:
         out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=ops.q8.device)
+    else:
+        _check_out(prob, out, ops.q8.device)
+    if lists is not None:
+        _check_lists(prob, lists, ops.q8.device, need_cap_nk=False)
     p = prob.c()
     o = ops.c()
     bl = lists.c() if lists is not None else None
@@ -264,6 +307,27 @@ class ClusterLists(NamedTuple):
     def c(self) -> _lib.AbsaClusterLists:
         return _lib.AbsaClusterLists(self.count.data_ptr(), self.kv_idx.data_ptr(), self.w.data_ptr(),
                                      self.label.data_ptr(), int(self.kv_idx.shape[1]), int(self.w.shape[2]))
+
+
+def _check_cluster_lists(prob: Problem, lists, device):
+    """Per-cluster lists: int32 count [rows], int32 kv_idx [rows, cap] with cap >= NK, fp32 w
+    [rows, cap, C], uint8 label [rows, Bq]; contiguous, on the inputs' GPU."""
+    import torch
+    count, kv_idx, w, label = lists
+    for t, dt, name in ((count, torch.int32, "count"), (kv_idx, torch.int32, "kv_idx"),
+                        (w, torch.float32, "w"), (label, torch.uint8, "label")):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_cuda or t.device != device:
+            raise ValueError(f"lists.{name} must be a {dt} tensor on the same GPU as Q and K")
+        if not t.is_contiguous():
+            raise ValueError(f"lists.{name} must be contiguous")
+    if tuple(count.shape) != (prob.rows,) or kv_idx.dim() != 2 or kv_idx.shape[0] != prob.rows:
+        raise ValueError(f"lists.count / kv_idx must be [rows] / [rows, cap] with rows = {prob.rows}")
+    if kv_idx.shape[1] < prob.nk:
+        raise ValueError(f"lists capacity {kv_idx.shape[1]} is below NK = {prob.nk}")
+    if w.dim() != 3 or tuple(w.shape[:2]) != tuple(kv_idx.shape):
+        raise ValueError("lists.w must be [rows, cap, C]")
+    if tuple(label.shape) != (prob.rows, prob.q_block):
+        raise ValueError(f"lists.label must be [rows, Bq] = {(prob.rows, prob.q_block)}")
 
 
 def alloc_cluster_lists(prob: Problem, clusters: int = 4, device="cuda") -> ClusterLists:
@@ -293,6 +357,7 @@ def select_clusters(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmea
     import torch
     _check_qkv(prob, q, k)
     lists = alloc_cluster_lists(prob, clusters, q.device) if lists is None else lists
+    _check_cluster_lists(prob, lists, q.device)
     nbytes = select_clusters_workspace_bytes(prob, keep, clusters, kmeans_steps, select_scale_log2, seed,
                                              stream_id, mode)
     if workspace is None or workspace.numel() < nbytes:
@@ -310,9 +375,12 @@ def attend_clusters(prob: Problem, q, k, v, lists: ClusterLists, out=None):
     """Attention over per-cluster lists (each query over its cluster's sample).  Returns O."""
     import torch
     _check_qkv(prob, q, k, v)
+    _check_cluster_lists(prob, lists, q.device)
     odt = torch.bfloat16 if prob.out_bf16 else torch.float32
     if out is None:
         out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    else:
+        _check_out(prob, out, q.device)
     p = prob.c()
     cl = lists.c()
     st = library().absa_attend_clusters(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),

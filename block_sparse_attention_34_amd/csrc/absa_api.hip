@@ -357,11 +357,19 @@ absa_status absa_select_clusters(const absa_problem* prob, const absa_select_par
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
 
+// The bf16 attention kernels address one head's K and V through 32-bit buffer
+// offsets, with 0x7FFFFFF0 as the out-of-range base of entries outside a list:
+// a head's L*d*2 bytes plus one 64-key tile must stay below it.
+static bool head_fits_buffer(const absa_problem* p) {
+  return (int64_t)p->L * p->d * 2 <= (int64_t)0x7FFFFFF0 - (int64_t)64 * p->d * 2;
+}
+
 static absa_status attend_common(const absa_problem* prob, const void* q, const void* k, const void* v,
                                  const absa_blocklist* lists, void* o, void* stream, bool dense) {
   Dims dm;
   absa_status st = check_problem(prob, &dm);
   if (st != ABSA_OK) return st;
+  if (!head_fits_buffer(prob)) return ABSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return ABSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
   if (!dense) {
@@ -408,6 +416,7 @@ absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const 
   Dims dm;
   absa_status st = check_problem(prob, &dm);
   if (st != ABSA_OK) return st;
+  if (!head_fits_buffer(prob)) return ABSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return ABSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
   if (prob->q_block != 128) return ABSA_ERR_UNSUPPORTED;

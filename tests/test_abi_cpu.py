@@ -170,6 +170,19 @@ def test_attend_and_dense_validation(lib):
         _lib.ABSA_ERR_INVALID_ARG
 
 
+def test_attend_rejects_heads_beyond_32bit_buffer_offsets(lib):
+    # the bf16 attention kernels address a head's K and V with 32-bit buffer offsets and use
+    # 0x7FFFFFF0 as the base of entries outside a list: L*d*2 + one 64-key tile must stay below it
+    big = prob(L=1 << 23, T=128, Hs=256, Ws=256, d=128, q_block=128)   # L*d*2 = 2^31
+    assert lib.absa_attend(ctypes.byref(big), FAKE, FAKE, FAKE, ctypes.byref(lists(cap=1 << 19)), FAKE, None) == \
+        _lib.ABSA_ERR_UNSUPPORTED
+    assert lib.absa_dense(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
+    assert lib.absa_attend_clusters(ctypes.byref(big), FAKE, FAKE, FAKE, ctypes.byref(cl_lists(cap=1 << 19)),
+                                    FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
+    big64 = prob(L=1 << 24, T=256, Hs=256, Ws=256, d=64, q_block=128)  # L*d*2 = 2^31 at d = 64
+    assert lib.absa_dense(ctypes.byref(big64), FAKE, FAKE, FAKE, FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
+
+
 def fp8_ops(**kw):
     base = dict(q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, kbar=FAKE, v8t=FAKE, sv=FAKE, mu=FAKE)
     base.update(kw)
