@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
 
 __all__ = [
-    "Problem", "BlockLists", "select", "attend", "dense", "num_blocks", "select_workspace_bytes",
+    "Problem", "BlockLists", "select", "select_noalloc", "attend", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
     "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
     "ClusterLists", "alloc_cluster_lists", "select_clusters_workspace_bytes", "select_clusters", "attend_clusters",
@@ -185,6 +185,29 @@ def select(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmeans_steps:
                                workspace.data_ptr(), workspace.numel(), _stream())
     _lib.check(st, "absa_select")
     return lists, pi, workspace
+
+
+def select_noalloc(prob: Problem, q, k, keep: float, lists: BlockLists, *, clusters: int = 0,
+                   kmeans_steps: int = 0, select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0,
+                   mode="sip", pi=None):
+    """``select`` into caller-given ``lists`` (and ``pi`` [rows, NK] fp32 if given) through
+    absa_select_noalloc: no workspace and no device allocation by this call; the library's fixed
+    64 MiB per-device scratch buffer holds the intermediates (calls overlapping on one device race).
+    Raises AbsaError(ABSA_ERR_TOO_LARGE) for problems whose workspace exceeds it."""
+    import torch
+    _check_qkv(prob, q, k)
+    _check_lists(prob, lists, q.device, need_cap_nk=True)
+    if pi is not None:
+        if (not isinstance(pi, torch.Tensor) or pi.dtype != torch.float32 or pi.device != q.device
+                or not pi.is_contiguous() or tuple(pi.shape) != (prob.rows, prob.nk)):
+            raise ValueError(f"pi must be a contiguous fp32 [rows, NK] = {(prob.rows, prob.nk)} tensor on Q's GPU")
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    bl = lists.c()
+    st = library().absa_select_noalloc(ctypes.byref(p), ctypes.byref(sp), q.data_ptr(), k.data_ptr(),
+                                       ctypes.byref(bl), pi.data_ptr() if pi is not None else None, _stream())
+    _lib.check(st, "absa_select_noalloc")
+    return lists, pi
 
 
 def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):

@@ -12,6 +12,7 @@ ABSA_ERR_UNSUPPORTED = -3
 ABSA_ERR_WORKSPACE = -4
 ABSA_ERR_HIP = -5
 ABSA_ERR_ALIGNMENT = -6
+ABSA_ERR_TOO_LARGE = -7
 
 SEL_SIP, SEL_TOPK, SEL_ALL = 0, 1, 2
 
@@ -20,6 +21,7 @@ EXPORTED = (
     "absa_select_workspace_layout", "absa_select", "absa_attend", "absa_dense",
     "absa_fp8_workspace", "absa_quantize_fp8", "absa_attend_fp8",
     "absa_select_clusters_workspace", "absa_select_clusters", "absa_attend_clusters",
+    "absa_select_noalloc",
 )
 
 
@@ -94,6 +96,8 @@ def load() -> ctypes.CDLL:
     lib.absa_select_workspace_layout.argtypes = [P, SP, ctypes.POINTER(sz)]
     lib.absa_select.restype = ctypes.c_int
     lib.absa_select.argtypes = [P, SP, vp, vp, BL, vp, vp, sz, vp]
+    lib.absa_select_noalloc.restype = ctypes.c_int
+    lib.absa_select_noalloc.argtypes = [P, SP, vp, vp, BL, vp, vp]
     lib.absa_attend.restype = ctypes.c_int
     lib.absa_attend.argtypes = [P, vp, vp, vp, BL, vp, vp]
     lib.absa_dense.restype = ctypes.c_int

@@ -7,6 +7,14 @@
 #include "absa.h"
 #include "absa_launch.h"
 
+// Fixed selection workspace of absa_select_noalloc, one copy per device
+// (module-scope device memory, held until the process ends).  Host code never
+// passes `scratch` itself to a kernel: on the host that name is only a stand-in
+// for the symbol, and its device address, different on every device, comes from
+// hipGetSymbolAddress with that device current (scratch_ptr below).
+static constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kMaxNK = 12288;  // selection keeps one row of scores in LDS
@@ -182,6 +190,28 @@ Fp8Ws fp8_ws(const Dims& dm) {
 std::once_flag g_attr_once;
 hipError_t g_attr_err = hipSuccess;
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per device.
+hipError_t scratch_ptr(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || !aligned(p, kWsAlign)) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,6 +227,7 @@ const char* absa_status_string(int32_t status) {
     case ABSA_ERR_WORKSPACE: return "workspace missing or too small";
     case ABSA_ERR_HIP: return "HIP runtime error";
     case ABSA_ERR_ALIGNMENT: return "misaligned pointer";
+    case ABSA_ERR_TOO_LARGE: return "problem needs more than the library's fixed scratch buffer (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -274,29 +305,32 @@ static absa::SelectLaunch select_launch(const absa_problem* prob, const absa_sel
   return a;
 }
 
-absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
-                        const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  Dims dm;
-  SelParams sp;
-  absa_status st = check_problem(prob, &dm);
+// Validation of absa_select's arguments other than the workspace; fills the
+// dimensions, parameters and workspace layout of a valid call.
+static absa_status check_select(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                const void* k, const absa_blocklist* out, const float* pi_out, Dims* dm,
+                                SelParams* sp, WsLayout* w) {
+  absa_status st = check_problem(prob, dm);
   if (st != ABSA_OK) return st;
-  st = check_params(prob, params, &sp);
+  st = check_params(prob, params, sp);
   if (st != ABSA_OK) return st;
   if (!q || !k) return ABSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16)) return ABSA_ERR_ALIGNMENT;
-  if (dm.NK > kMaxNK) return ABSA_ERR_UNSUPPORTED;
-  st = check_lists(out, true, dm.NK);
+  if (dm->NK > kMaxNK) return ABSA_ERR_UNSUPPORTED;
+  st = check_lists(out, true, dm->NK);
   if (st != ABSA_OK) return st;
   if (pi_out && !aligned(pi_out, 4)) return ABSA_ERR_ALIGNMENT;
-  const WsLayout w = ws_layout(prob, dm, sp.C);
-  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
-  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+  *w = ws_layout(prob, *dm, sp->C);
+  return ABSA_OK;
+}
 
+// The launches of one selection call into a checked workspace.
+static absa_status run_select(const absa_problem* prob, const absa_select_params* params, const Dims& dm,
+                              const SelParams& sp, const WsLayout& w, const void* q, const void* k,
+                              const absa_blocklist* out, float* pi_out, char* workspace, void* stream) {
   std::call_once(g_attr_once, [] { g_attr_err = absa::configure_select_kernels(); });
   if (g_attr_err != hipSuccess) return ABSA_ERR_HIP;
-
-  absa::SelectLaunch a = select_launch(prob, params, dm, sp, w, static_cast<char*>(workspace), q, k);
+  absa::SelectLaunch a = select_launch(prob, params, dm, sp, w, workspace, q, k);
   a.count = out->count;
   a.kv_idx = out->kv_idx;
   a.inv_pi = out->inv_pi;
@@ -304,6 +338,32 @@ absa_status absa_select(const absa_problem* prob, const absa_select_params* para
   a.pi_out = pi_out;
   hipError_t e = absa::launch_select(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
+absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
+                        const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Dims dm;
+  SelParams sp;
+  WsLayout w;
+  absa_status st = check_select(prob, params, q, k, out, pi_out, &dm, &sp, &w);
+  if (st != ABSA_OK) return st;
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+  return run_select(prob, params, dm, sp, w, q, k, out, pi_out, static_cast<char*>(workspace), stream);
+}
+
+absa_status absa_select_noalloc(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                const void* k, const absa_blocklist* out, float* pi_out, void* stream) {
+  Dims dm;
+  SelParams sp;
+  WsLayout w;
+  absa_status st = check_select(prob, params, q, k, out, pi_out, &dm, &sp, &w);
+  if (st != ABSA_OK) return st;
+  if (w.total > kScratchBytes) return ABSA_ERR_TOO_LARGE;
+  char* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return ABSA_ERR_HIP;
+  return run_select(prob, params, dm, sp, w, q, k, out, pi_out, ws, stream);
 }
 
 absa_status absa_select_clusters_workspace(const absa_problem* prob, const absa_select_params* params,

@@ -47,7 +47,8 @@
  *   - A "row" is one (b, h, query block) triple; rows are ordered
  *     (b*H + h)*NQ + i.
  *   - The caller allocates and owns every buffer; the library allocates no
- *     device memory and keeps no mutable global state.
+ *     device memory and keeps no mutable global state (the one exception is
+ *     the fixed module-scope buffer of absa_select_noalloc, below).
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL is the null
  *     stream) and never synchronise.  Results are valid once the caller
  *     synchronises with that stream.
@@ -74,7 +75,9 @@ typedef enum absa_status {
   ABSA_ERR_UNSUPPORTED = -3, /* valid but not implemented (d, block sizes, C)   */
   ABSA_ERR_WORKSPACE = -4,   /* workspace missing or too small                  */
   ABSA_ERR_HIP = -5,         /* a HIP runtime call or a launch failed           */
-  ABSA_ERR_ALIGNMENT = -6    /* a pointer is not aligned as required            */
+  ABSA_ERR_ALIGNMENT = -6,   /* a pointer is not aligned as required            */
+  ABSA_ERR_TOO_LARGE = -7    /* needs more than absa_select_noalloc's fixed
+                                64 MiB scratch buffer                           */
 } absa_status;
 
 typedef enum absa_sel_mode {
@@ -150,6 +153,22 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
 absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
                         const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* absa_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops, harnesses
+ * that forbid allocation).  The selection workspace is a fixed 64 MiB buffer in
+ * the library's module-scope device memory, one per device, set up on the
+ * first call on that device and held until the process ends; this call itself
+ * allocates nothing.  Problems whose workspace (absa_select_workspace) exceeds
+ * 64 MiB return ABSA_ERR_TOO_LARGE before any launch.  Outputs, arguments and
+ * errors are those of absa_select; the buffer's intermediates are not
+ * published.  Every call on one device shares that device's buffer: calls
+ * whose work overlaps on one device (on different streams, or from several
+ * threads without ordering) race and give undefined lists; calls on one
+ * stream are ordered and safe.  A failed lookup of the buffer returns
+ * ABSA_ERR_HIP. */
+absa_status absa_select_noalloc(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                const void* k, const absa_blocklist* out, float* pi_out, void* stream);
 
 /* Block-sparse attention over given lists (the estimate above): for every
  * valid query of row r, attends to the keys of the blocks listed for r with

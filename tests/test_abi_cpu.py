@@ -183,6 +183,25 @@ def test_attend_rejects_heads_beyond_32bit_buffer_offsets(lib):
     assert lib.absa_dense(ctypes.byref(big64), FAKE, FAKE, FAKE, FAKE, None) == _lib.ABSA_ERR_UNSUPPORTED
 
 
+def test_select_noalloc_validation(lib):
+    P, S = ctypes.byref(prob()), ctypes.byref(params())
+    call = lib.absa_select_noalloc
+    assert lib.absa_status_string(_lib.ABSA_ERR_TOO_LARGE).startswith(b"problem needs more")
+    assert call(P, S, None, FAKE, ctypes.byref(lists()), None, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert call(P, S, FAKE + 8, FAKE, ctypes.byref(lists()), None, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists(cap=63)), None, None) == _lib.ABSA_ERR_SHAPE
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE + 1, None) == _lib.ABSA_ERR_ALIGNMENT
+    # the workspace of the 720p Wan shape with 2 heads (120 MiB) exceeds the fixed 64 MiB buffer
+    p2 = prob(H=2, L=75600, T=21, Hs=45, Ws=80, d=128, q_block=128)
+    n = ctypes.c_size_t()
+    assert lib.absa_select_workspace(ctypes.byref(p2), S, ctypes.byref(n)) == 0 and n.value > 64 << 20
+    assert call(ctypes.byref(p2), S, FAKE, FAKE, ctypes.byref(lists(cap=4725)), None, None) == \
+        _lib.ABSA_ERR_TOO_LARGE
+    import torch
+    if not torch.cuda.is_available():   # a valid call reaches its first HIP call, which fails here
+        assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), None, None) == _lib.ABSA_ERR_HIP
+
+
 def fp8_ops(**kw):
     base = dict(q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, kbar=FAKE, v8t=FAKE, sv=FAKE, mu=FAKE)
     base.update(kw)
