@@ -47,5 +47,16 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_test_probe(src: str, out: str) -> str:
+    """Compile one test-support HIP source (not part of the library) into a shared object."""
+    tmp = out + ".tmp"
+    cmd = [hipcc_path()] + HIPCC_FLAGS + ["-o", tmp, src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr[-8000:])
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

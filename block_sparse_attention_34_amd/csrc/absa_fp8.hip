@@ -657,13 +657,17 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
     return mt;
   };
   // raise the integer reference when the tile holds a y above 120 (or on the
-  // first tile with a finite logit) so that the tile's max lands two octaves
-  // below that limit: y -= 8 step, O and l scale by 2^-step
+  // first tile with a finite logit) by the fewest whole octaves that bring the
+  // tile's max to 120 or below: y -= 8 step, O and l scale by 2^-step.  The
+  // reference so reached is the smallest integer that keeps every y of the row
+  // at or below 120, whatever the order of the tiles; a term computed under an
+  // earlier, lower reference keeps its byte's value exactly after the rescale
+  // unless that byte falls below the normal range under the final one.
   auto rescale = [&](float mt, float m_use) {
     mt = half_swap_max(mt);
     const bool need = mt > 120.f || (m_run == -INFINITY && mt > -INFINITY);
     if (__ballot(need) != 0ull) {
-      const float step = need ? ceilf((mt - 120.f) * 0.125f) + 2.f : 0.f;
+      const float step = need ? ceilf((mt - 120.f) * 0.125f) : 0.f;
       const float alpha = need ? ((m_run == -INFINITY) ? 0.f : ldexpf(1.f, -(int)step)) : 1.f;
       l_run *= alpha;
 #pragma unroll

@@ -242,11 +242,16 @@ absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const 
  *   V      mu_hat[b][c] = bf16(fp32(mean of block b's valid keys)); residual
  *          r = v - mu_hat (fp32); per channel c of the head: s_V[c] from
  *          max_t |r[t][c]|, code = e4m3_rne(r / s_V);
- *   P      y = 8 (l - m) + 120 in fp32 with l = scale log2(e) s_Q s_K (q8.k8)
- *          + log2 w_b and m an integer reference that rises by
- *          ceil((max y - 120) / 8) + 2 whenever a 64-key tile (four list
- *          entries, in list order) holds a y above 120; p = e4m3 value of the
- *          byte sat_u8(rne(y));
+ *   P      y = 8 (l - m) + 120 in fp32 (one fused multiply-add from the dot
+ *          product of the codes) with l = scale log2(e) s_Q s_K (q8.k8)
+ *          + log2 w_b and m, per query, the smallest integer that keeps
+ *          every y of the row's kept keys at or below 120 (so m = ceil(max l)
+ *          up to the roundings of y, independent of the list's order);
+ *          p = e4m3 value of the byte sat_u8(rne(y)).  The kernel reaches m
+ *          through a running reference that rises by whole octaves, so a term
+ *          formed under an earlier, lower reference can differ from its value
+ *          under m only below E4M3's normal range (bytes < 8, more than 14
+ *          octaves under the row's largest term);
  *   O      o_t = sum_k p_k (mu_hat + s_V dec(code_k)) / sum_k p_k (0 for an
  *          empty list).
  *   QK     optionally INT8 instead of E4M3 (the page builds on earlier 8-bit

@@ -33,19 +33,23 @@ F3  V: per KV block the mean of its valid keys, rounded to bf16 (mu_hat); the
     reconstructed for key t of block b is mu_hat_b + s_V * dec(code).
 F4  Logits in log2 units: y = 8 (l - m) + 120 with l = sigma log2(e) s_Q s_K
     (q8 . k8) + log2 w_b, formed in fp32 by one fused multiply-add from the
-    exact dot product of the codes.  The reference m is an integer: the keys of
-    a row are taken in tiles of 64 (four 16-key list entries, in list order;
-    the dense case takes consecutive 64-key tiles); whenever a tile holds a y
-    above 120 (or on the first tile with a finite logit) m rises by
-    ceil((max y - 120) / 8) + 2, which leaves the tile's max two octaves below
-    the limit so that the reference moves seldom, and the earlier sums are
-    scaled by 2^-(that step).
+    exact dot product of the codes: y = fp32(dot * M + c) with M = 8 fp32(sigma
+    log2 e) s_Q s_K (exact: the scales are powers of two) and c = fp32(8
+    fp32(fp32(log2 w) - m) + 120).  The reference m is one integer per query,
+    fixed over the row's whole kept set: the smallest integer for which every
+    kept key has y <= 120 (so the largest logit lands in (112, 120] and m =
+    ceil(max l) up to the fp32 roundings of y).  It depends on the set of kept
+    keys only, not on their order, and no running reference or rescaling
+    enters the definition.
 F5  ExpCast: p = dec_e4m3(sat_u8(rne(y))), the byte being y rounded to the
     nearest integer (ties to even) and clamped to [0, 255]; y <= 120 keeps it
     finite.  For bytes in the normal range 2^m dec(byte) does not depend on
-    the integer m, so p is a fixed function of l (within 1.0615x of 2^l).
+    the integer m, so p is a fixed function of l (within 1.0615x of 2^l);
+    bytes below 8 (y below 7.5) are E4M3 subnormals or zero, the underflow
+    floor about 14 octaves below the largest term.
 F6  o_t = sum_k p_k (mu_hat_b(k) + s_V dec(code_k)) / sum_k p_k over the row's
-    kept keys (weights through log2 w inside l); an empty list gives 0.
+    kept keys (weights through log2 w inside l), the sums taken in ascending
+    key order whatever the order of the list; an empty list gives 0.
 F7  QK in INT8 instead (the page takes the QK side from earlier low-bit
     kernels such as SageAttention2, which smooth K and quantise QK to 8-bit
     integers): the same per-token Q and smoothed per-block K scaling with 127
@@ -59,7 +63,7 @@ that only accumulate are fp64.
 from __future__ import annotations
 
 import math
-from typing import Optional, Sequence, Tuple
+from typing import NamedTuple, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -68,13 +72,12 @@ from .absa_oracle import num_blocks, valid_len
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "bf16_round", "pow2_scale",
     "quantize_q", "smooth_k", "quantize_k", "quantize_v", "Fp8Head", "I8_MAX", "pow2_scale_i8", "i8_encode",
-    "quantize_head", "expcast_p", "attend_row_fp8", "attend_all_fp8",
+    "quantize_head", "expcast_p", "Fp8RowTerms", "fp8_row_terms", "attend_row_fp8", "attend_all_fp8",
 ]
 
 E4M3_MAX = 448.0
 I8_MAX = 127.0
 EXPCAST_OFFSET = 120.0  # F4: the byte of the reference value 2^0 (a multiple of 8)
-RESCALE_HEADROOM = 2.0  # F4: octaves left above a tile's max after the reference moves
 
 _F32 = np.float32
 
@@ -241,60 +244,92 @@ def expcast_p(y) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- F4-F6
 
+class Fp8RowTerms(NamedTuple):
+    """The per-key terms of F4-F6 for a block of queries: keys in ascending order."""
+    keys: np.ndarray     # [nk] int64 key indices
+    dot: np.ndarray      # [n, nk] exact dot products q8 . k8 of the code values
+    absdot: np.ndarray   # [n, nk] sum_i |q8_i k8_i| (the size of the dot product's terms)
+    mul: np.ndarray      # [n, nk] M = 8 fp32(sigma log2 e) s_Q s_K
+    add: np.ndarray      # [n, nk] c = fp32(8 fp32(fp32(log2 w) - m) + 120)
+    m: np.ndarray        # [n] the integer reference of each query (F4)
+    y: np.ndarray        # [n, nk] fp32 y
+    p: np.ndarray        # [n, nk] F5 probabilities (fp64 values of E4M3 bytes)
+    vals: np.ndarray     # [nk, d] reconstructed V (F3)
+    mean: np.ndarray     # [nk, d] mu_hat of each key's block (the block-mean part of vals)
+
+
+def _y_at(dot, mul, lw32, m) -> np.ndarray:
+    """F4: fp32 y at integer references m [n] for all keys."""
+    c = (lw32[None, :] - m.astype(_F32)[:, None]).astype(_F32)
+    add = (c * _F32(8.0)).astype(np.float64) + EXPCAST_OFFSET
+    add = add.astype(_F32).astype(np.float64)
+    return (dot * mul + add).astype(_F32).astype(np.float64), add
+
+
+def fp8_row_terms(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequence[float], sigma: float,
+                  dense: bool = False) -> Optional[Fp8RowTerms]:
+    """F4-F5 for queries t0 .. t0+n-1 of one head over the kept keys (every key with weight 1 if
+    ``dense``); None for an empty list."""
+    L, Bk = hd.L, hd.Bk
+    if dense:
+        blocks = np.arange(num_blocks(L, Bk), dtype=np.int64)
+        wts = np.ones(blocks.size)
+    else:
+        if len(kept) == 0:
+            return None
+        order = np.argsort(np.asarray(kept, dtype=np.int64), kind="stable")   # the list is a set
+        blocks = np.asarray(kept, dtype=np.int64)[order]
+        wts = np.asarray(w, dtype=np.float64)[order]
+    keys, lw = [], []
+    for b, wb in zip(blocks, wts):
+        nb = valid_len(int(b), Bk, L)
+        keys.extend(range(int(b) * Bk, int(b) * Bk + nb))
+        lw.extend([math.log2(float(wb))] * nb)
+    keys = np.asarray(keys, dtype=np.int64)
+    lw32 = np.asarray(lw, dtype=np.float64).astype(_F32)
+    blk = keys // Bk
+    sl2 = _F32(sigma * math.log2(math.e))
+    qv = hd.qk_values(hd.q8[t0:t0 + n])
+    kv = hd.qk_values(hd.k8[keys])
+    dot = qv @ kv.T                                          # exact
+    absdot = np.abs(qv) @ np.abs(kv).T
+    mul = ((sl2 * hd.sq[t0:t0 + n]).astype(_F32)[:, None] * hd.sk[blk][None, :]).astype(_F32) * _F32(8.0)
+    mul = mul.astype(np.float64)                             # exact products of powers of two and sl2
+    # F4 reference: the smallest integer m with max_k y_k(m) <= 120; y(m) does not increase with m,
+    # and ceil(max l) - 1 is below it (the fp32 roundings move y by far less than 8)
+    lmax = (dot * mul / 8.0 + lw32[None, :]).max(axis=1)
+    m = np.ceil(lmax) - 2.0
+    for _ in range(6):
+        y, _ = _y_at(dot, mul, lw32, m)
+        over = y.max(axis=1) > EXPCAST_OFFSET
+        if not over.any():
+            break
+        m = np.where(over, m + 1.0, m)
+    y, add = _y_at(dot, mul, lw32, m)
+    if (y.max(axis=1) > EXPCAST_OFFSET).any():
+        raise AssertionError("F4 reference search did not settle")
+    down, _ = _y_at(dot, mul, lw32, m - 1.0)
+    if not (down.max(axis=1) > EXPCAST_OFFSET).all():
+        raise AssertionError("F4 reference is not the smallest admissible integer")
+    return Fp8RowTerms(keys=keys, dot=dot, absdot=absdot, mul=mul, add=add, m=m, y=y, p=expcast_p(y),
+                       vals=hd.values()[keys], mean=hd.mu.astype(np.float64)[blk])
+
+
 def attend_row_fp8(hd: Fp8Head, t0: int, n: int, kept: Sequence[int], w: Sequence[float],
                    sigma: float, dense: bool = False, expcast: bool = True) -> np.ndarray:
     """F4-F6 output [n, d] for queries t0 .. t0+n-1 of one head given its block list.
 
-    With ``dense`` the list is ignored and every key is kept with weight 1
-    (consecutive 64-key tiles).  ``expcast=False`` replaces the F5 byte by the
-    exact power 2^((y - 120) / 8) (used to check the rest of the assembly).
+    With ``dense`` the list is ignored and every key is kept with weight 1.  ``expcast=False``
+    replaces the F5 byte by the exact power 2^((y - 120) / 8) (used to check the rest of the
+    assembly).
     """
-    L, Bk = hd.L, hd.Bk
     d = hd.q8.shape[1]
-    sl2 = _F32(sigma * math.log2(math.e))
-    q8v = hd.qk_values(hd.q8[t0:t0 + n])                     # [n, d] exact
-    qsc = (sl2 * hd.sq[t0:t0 + n]).astype(_F32)              # fp32 per query
-    vals = hd.values()
-    if dense:
-        tiles = [list(range(s, min(s + 64, L))) for s in range(0, L, 64)]
-        tile_keys = [(np.array(t), np.zeros(len(t))) for t in tiles]
-    else:
-        if len(kept) == 0:
-            return np.zeros((n, d))
-        spt = 64 // Bk
-        tile_keys = []
-        for s in range(0, len(kept), spt):
-            ks, bs = [], []
-            for b, wb in zip(kept[s:s + spt], w[s:s + spt]):
-                b = int(b)
-                nb = valid_len(b, Bk, L)
-                ks.extend(range(b * Bk, b * Bk + nb))
-                bs.extend([math.log2(float(wb))] * nb)
-            tile_keys.append((np.array(ks, dtype=np.int64), np.array(bs)))
-    num = np.zeros((n, d))
-    den = np.zeros(n)
-    m = np.full(n, -np.inf)
-    for keys, bias in tile_keys:
-        if keys.size == 0:
-            continue
-        blk = keys // Bk
-        acc = q8v @ hd.qk_values(hd.k8[keys]).T              # exact dot products [n, nk]
-        sc8 = (qsc[:, None] * hd.sk[blk][None, :]).astype(_F32) * _F32(8.0)
-        m_use = np.where(np.isinf(m), 0.0, m)
-        cb = (bias.astype(_F32)[None, :] - m_use.astype(_F32)[:, None]).astype(_F32)
-        cb8 = cb * _F32(8.0) + _F32(EXPCAST_OFFSET)
-        y = (acc * sc8.astype(np.float64) + cb8.astype(np.float64)).astype(_F32).astype(np.float64)
-        ymax = y.max(axis=1)
-        need = (ymax > EXPCAST_OFFSET) | (np.isinf(m) & np.isfinite(ymax))
-        step = np.where(need, np.ceil((ymax - EXPCAST_OFFSET) / 8.0) + RESCALE_HEADROOM, 0.0)
-        alpha = np.where(need & ~np.isinf(m), 2.0 ** -step, np.where(need, 0.0, 1.0))
-        num *= alpha[:, None]
-        den *= alpha
-        m = np.where(need, m_use + step, m)
-        y = y - 8.0 * step[:, None]
-        p = expcast_p(y) if expcast else 2.0 ** ((y - EXPCAST_OFFSET) / 8.0)
-        num += p @ vals[keys]
-        den += p.sum(axis=1)
+    t = fp8_row_terms(hd, t0, n, kept, w, sigma, dense)
+    if t is None:
+        return np.zeros((n, d))
+    p = t.p if expcast else 2.0 ** ((t.y - EXPCAST_OFFSET) / 8.0)
+    num = p @ t.vals
+    den = p.sum(axis=1)
     out = np.zeros((n, d))
     nz = den > 0
     out[nz] = num[nz] / den[nz][:, None]

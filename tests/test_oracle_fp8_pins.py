@@ -175,10 +175,9 @@ def test_assembly_equals_S6_estimator_on_exact_inputs():
     np.testing.assert_allclose(got, num / den[:, None], rtol=2e-5, atol=2e-5)
 
 
-def test_tile_order_does_not_change_the_output():
-    # F4/F5: the integer reference moves by whole octaves, so a different tile order (a different
-    # sequence of references and rescales) gives the same p, except where the fp32 rounding of y
-    # (whose ulp depends on the reference) moves a byte across a rounding boundary.
+def test_list_order_does_not_change_the_output():
+    # F4/F6: the reference is fixed over the row's whole kept set and the sums run in ascending key
+    # order, so any permutation of a list (a set of blocks with their weights) gives the same bytes
     rng = np.random.default_rng(4)
     L, d, Bk = 512, 32, 16
     q = rng.standard_normal((L, d)).astype(np.float32)
@@ -186,19 +185,70 @@ def test_tile_order_does_not_change_the_output():
     v = rng.standard_normal((L, d)).astype(np.float32)
     hd = O.Fp8Head(q, k, v, Bk)
     kept = list(range(0, 32, 1))
-    w = list(2.0 ** rng.integers(0, 3, len(kept)))
+    w = list(2.0 ** rng.integers(0, 3, len(kept)) * rng.uniform(1.0, 1.5, len(kept)))
     a = O.attend_row_fp8(hd, 0, 40, kept, w, 0.2)
-    perm = rng.permutation(len(kept))
-    b = O.attend_row_fp8(hd, 0, 40, [kept[i] for i in perm], [w[i] for i in perm], 0.2)
-    # most rows (queries) match to fp64 rounding (elements near the floor, below 2^-11 of the
-    # reference, and fp32 ties are treated per path); a wrong rescale factor would move every row
-    # by far more than 1e-3
-    same = np.isclose(a, b, rtol=1e-12, atol=1e-12).all(axis=1)
-    assert same.mean() >= 0.7
-    np.testing.assert_allclose(a, b, rtol=0, atol=1e-3 * np.abs(a).max())
-    c = O.attend_row_fp8(hd, 0, 40, kept[::-1], w[::-1], 0.2)
-    assert np.isclose(a, c, rtol=1e-12, atol=1e-12).all(axis=1).mean() >= 0.7
-    np.testing.assert_allclose(a, c, rtol=0, atol=1e-3 * np.abs(a).max())
+    for trial in range(3):
+        perm = rng.permutation(len(kept))
+        b = O.attend_row_fp8(hd, 0, 40, [kept[i] for i in perm], [w[i] for i in perm], 0.2)
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a, O.attend_row_fp8(hd, 0, 40, kept[::-1], w[::-1], 0.2))
+
+
+def test_reference_is_the_smallest_admissible_integer():
+    # F4: per query, every y <= 120 and one octave down (m - 1) some y would exceed 120; the largest
+    # term's byte therefore lies in [112, 120] and m = ceil(max l) wherever max l is not within the
+    # fp32 roundings of an integer
+    rng = np.random.default_rng(12)
+    L, d, Bk = 384, 64, 16
+    q = O.bf16_round(rng.standard_normal((L, d)).astype(np.float32) * 3)
+    k = O.bf16_round(rng.standard_normal((L, d)).astype(np.float32))
+    v = O.bf16_round(rng.standard_normal((L, d)).astype(np.float32))
+    for qk_int8 in (False, True):
+        hd = O.Fp8Head(q, k, v, Bk, qk_int8=qk_int8)
+        kept = [1, 4, 5, 9, 17, 23]
+        w = [1.0, 3.0, 1.25, 7.5, 2.0, 1.0]
+        t = O.fp8_row_terms(hd, 64, 64, kept, w, 0.125)
+        ymax = t.y.max(axis=1)
+        assert np.all(ymax <= 120.0) and np.all(ymax >= 112.0 - 1e-3)
+        l = t.dot * t.mul / 8.0 + np.log2(np.repeat(np.asarray(w), 16))[None, :]
+        lmax = l.max(axis=1)
+        clear = np.abs(lmax - np.round(lmax)) > 1e-3
+        assert clear.sum() > 50
+        np.testing.assert_array_equal(t.m[clear], np.ceil(lmax[clear]))
+        # bytes of the largest terms: 112..120, the byte of 2^0 relative to the reference being 120
+        assert np.all(np.rint(ymax) >= 112) and np.all(np.rint(ymax) <= 120)
+
+
+def test_power_of_two_weights_shift_the_reference_only():
+    # F4/F5: scaling every weight by 2^j shifts every l and the reference by j and leaves each y,
+    # hence each byte and the output, unchanged; scaling one weight by 2 moves that block's bytes
+    # up by exactly 8 (one E4M3 octave) where they stay normal
+    rng = np.random.default_rng(13)
+    L, d, Bk = 256, 32, 16
+    q = rng.standard_normal((L, d)).astype(np.float32)
+    k = rng.standard_normal((L, d)).astype(np.float32)
+    v = rng.standard_normal((L, d)).astype(np.float32)
+    hd = O.Fp8Head(q, k, v, Bk)
+    kept = [0, 3, 6, 7, 11, 15]
+    w = [1.0, 2.0, 4.0, 1.0, 8.0, 2.0]
+    base = O.fp8_row_terms(hd, 0, 32, kept, w, 0.3)
+    for j in (1, 5, 13):
+        sh = O.fp8_row_terms(hd, 0, 32, kept, [x * 2.0 ** j for x in w], 0.3)
+        np.testing.assert_array_equal(sh.m, base.m + j)
+        np.testing.assert_array_equal(sh.y, base.y)
+        np.testing.assert_array_equal(sh.p, base.p)
+    w2 = list(w)
+    w2[1] *= 2.0                                     # block 3 (keys 48..63 in ascending order)
+    two = O.fp8_row_terms(hd, 0, 32, kept, w2, 0.3)
+    same = two.m == base.m                          # queries whose largest term is elsewhere
+    assert same.sum() >= 16
+    cols = slice(16, 32)
+    b0, b1 = np.rint(base.y[same][:, cols]), np.rint(two.y[same][:, cols])
+    normal = b0 >= 8
+    assert normal.sum() > 100
+    np.testing.assert_array_equal(b1[normal], b0[normal] + 8)
+    others = np.r_[0:16, 32:base.y.shape[1]]
+    np.testing.assert_array_equal(two.y[same][:, others], base.y[same][:, others])
 
 
 def test_key_shift_invariance_and_dense_equals_full_list():
