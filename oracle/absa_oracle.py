@@ -61,8 +61,8 @@ __all__ = [
     "kv_block_means", "ibcs_kmeans", "ibcs_scores",
     "sip_inclusion", "bisection_inclusion",
     "philox4x32_10", "sip_uniforms",
-    "select_row", "select", "SelectResult",
-    "estimator_num_den", "attend_row_block", "attend_rows", "attend_all",
+    "select_row", "select", "SelectResult", "selection_fp32_exact",
+    "estimator_num_den", "attend_row_block", "attend_rows", "attend_all", "sip_output_moments",
 ]
 
 SEL_SIP, SEL_TOPK, SEL_ALL = 0, 1, 2
@@ -347,6 +347,122 @@ def select(q: np.ndarray, k: np.ndarray, Bq: int, Bk: int, keep: float, C: int =
                         scores=scores, mu=mus, counts=cnts, kbar=kbar)
 
 
+# ----------------------------------------------------------------------------- exactness guard
+
+def _f32_exact(x) -> bool:
+    x = np.asarray(x, dtype=np.float64)
+    return bool(np.all(x.astype(np.float32).astype(np.float64) == x))
+
+
+def _split_bf16_exact(x) -> bool:
+    """x equals bf16(x) + bf16(x - bf16(x)) (16 significant bits in two bf16 halves)."""
+    x = np.asarray(x, dtype=np.float64).astype(np.float32)
+
+    def bf(a):
+        u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+        return u.astype(np.uint32).view(np.float32)
+    hi = bf(x)
+    lo = bf((x - hi).astype(np.float32))
+    return bool(np.all(hi.astype(np.float64) + lo.astype(np.float64) == x.astype(np.float64)))
+
+
+def _granule(x: float) -> float:
+    """The largest power of two dividing the positive float x."""
+    m, e = math.frexp(x)                 # x = m 2^e, m in [0.5, 1)
+    M = int(m * 2.0 ** 53)               # exact 53-bit integer
+    tz = (M & -M).bit_length() - 1
+    return math.ldexp(1.0, e - 53 + tz)
+
+
+def _sums_exact(terms: np.ndarray) -> bool:
+    """Every partial sum of the non-negative ``terms``, in any order, is exact in fp32: all are
+    multiples of the smallest granule among them and the total stays below 2^24 of it."""
+    t = np.asarray(terms, dtype=np.float64)
+    t = t[t > 0]
+    if t.size == 0:
+        return True
+    g = min(_granule(float(x)) for x in t)
+    return bool(t.sum() < g * 2.0 ** 24)
+
+
+def selection_fp32_exact(X: np.ndarray, kbar: np.ndarray, nk: np.ndarray, C: int, Tk: int, alpha: float,
+                         n_star: float) -> Tuple[bool, bool]:
+    """Exactness guard for the bit-exact selection tests (not a step of the method).
+
+    Re-runs S2-S4 on one query block X [n,d] against the block means kbar [NK,d] and reports
+    (exact, moved): ``exact`` when every intermediate a float32 implementation forms is exactly
+    representable, so that float32 arithmetic in any summation order (with correctly rounded
+    divisions and exact powers of two) reproduces the fp64 values and decisions of this oracle:
+    the centroids of every step (also as two bf16 halves, the operands of a split-bf16 product),
+    |mu|^2 and mu . x, every logit (an integer, so 2^(l - m) is exact), every term, normaliser and
+    partial sum of S3, the mixture coefficients n_j / n / Z_j, every score, and every S_U and
+    s_b R of the capping rounds.  ``moved``: the centroids still changed after the first step.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    n = X.shape[0]
+    if not (_f32_exact(X) and _f32_exact(kbar) and _f32_exact(n_star)):
+        return False, False
+    mu = np.stack([X[(j * n) // C] for j in range(C)])
+    counts = np.zeros(C, dtype=np.int64)
+    moved = False
+    for step in range(Tk):
+        if not (_f32_exact(mu) and _split_bf16_exact(mu)):
+            return False, moved
+        sq = (mu * mu).sum(axis=1)
+        G = X @ mu.T
+        if not (_f32_exact(sq) and _f32_exact(G) and _f32_exact(sq[None, :] - 2.0 * G)):
+            return False, moved
+        dist = ((X[:, None, :] - mu[None, :, :]) ** 2).sum(axis=2)
+        labels = np.argmin(dist, axis=1)
+        counts = np.bincount(labels, minlength=C)
+        new_mu = mu.copy()
+        for j in range(C):
+            if counts[j] > 0:
+                tot = X[labels == j].sum(axis=0)
+                if not _f32_exact(tot):
+                    return False, moved
+                new_mu[j] = tot / counts[j]
+        if step >= 1 and not np.array_equal(new_mu, mu):
+            moved = True
+        mu = new_mu
+    if not (_f32_exact(mu) and _split_bf16_exact(mu)):
+        return False, moved
+    s = np.zeros(kbar.shape[0])
+    for j in range(C):
+        if counts[j] == 0:
+            continue
+        logit = alpha * (np.asarray(kbar, dtype=np.float64) @ mu[j])
+        if not (_f32_exact(logit) and np.all(logit == np.round(logit))):
+            return False, moved
+        delta = logit - logit.max()
+        e = np.where(delta >= SCORE_FLOOR_LOG2, nk * np.exp2(delta), 0.0)
+        Z = e.sum()
+        coef = (counts[j] / n) / Z
+        if not (_sums_exact(e) and _f32_exact(counts[j] / n) and _f32_exact(coef) and _f32_exact(coef * e)):
+            return False, moved
+        s += coef * e
+        if not _f32_exact(s):
+            return False, moved
+    if not _sums_exact(s):
+        return False, moved
+    if n_star < s.shape[0]:
+        U = s > 0
+        R = float(n_star)
+        while True:
+            S_U = s[U].sum()
+            if not (_f32_exact(S_U) and _f32_exact(s[U] * R) and _f32_exact(R)):
+                return False, moved
+            N = U & (s * R >= S_U)
+            if not N.any():
+                break
+            U &= ~N
+            R -= int(N.sum())
+            if not U.any():
+                break
+    return True, moved
+
+
 # ----------------------------------------------------------------------------- S6 ([AB] SIP)
 
 def estimator_num_den(qb: np.ndarray, k: np.ndarray, v: np.ndarray, kept: Sequence[int],
@@ -419,3 +535,55 @@ def attend_all(q, k, v, Bq: int, Bk: int, count: np.ndarray, kv_idx: np.ndarray,
         blk = attend_row_block(q, k, v, bh, i, Bq, Bk, kv_idx[r, :c], inv_pi[r, :c], sigma)
         o[b, h, i * Bq: i * Bq + blk.shape[0]] = blk
     return o
+
+
+def sip_output_moments(qb: np.ndarray, k: np.ndarray, v: np.ndarray, pi_hat: np.ndarray, Bk: int,
+                       sigma: float, max_free: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """First and second moments of the S6 output over the S5 Poisson draws of one row.
+
+    pi_hat [NK] are the row's fp32 inclusion probabilities; block b is kept with probability
+    pi_hat_b, independently, and then carries the weight fp32(1 / pi_hat_b) (S5).  Blocks with
+    pi_hat 0 or 1 are fixed; the others (at most ``max_free``) are enumerated: every subset S
+    has probability prod_{b in S} pi_b prod_{b not in S} (1 - pi_b), and o(S) is the S6 ratio
+    (0 for an empty S).  Returns (E[o], E[o^2]) per element, [n, d] each.
+    """
+    qb = np.asarray(qb, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    pi = np.asarray(pi_hat, dtype=np.float32).astype(np.float64)
+    L, NK = k.shape[0], pi.shape[0]
+    w = np.zeros(NK)
+    w[pi > 0] = (1.0 / pi[pi > 0]).astype(np.float32).astype(np.float64)
+    a = sigma * (qb @ k.T)                                  # [n, L]
+    shift = a.max(axis=1, keepdims=True)
+    e = np.exp(a - shift)
+    n, d = qb.shape[0], v.shape[1]
+    Nb = np.zeros((NK, n, d))
+    Db = np.zeros((NK, n))
+    for b in range(NK):
+        t0, t1 = b * Bk, b * Bk + valid_len(b, Bk, L)
+        Nb[b] = w[b] * (e[:, t0:t1] @ v[t0:t1])
+        Db[b] = w[b] * e[:, t0:t1].sum(axis=1)
+    fixed = np.flatnonzero(pi >= 1.0)
+    free = np.flatnonzero((pi > 0.0) & (pi < 1.0))
+    if free.size > max_free:
+        raise ValueError("too many free blocks to enumerate")
+    m1 = np.zeros((n, d))
+    m2 = np.zeros((n, d))
+    Nf = Nb[free].reshape(free.size, n * d)
+    Df = Db[free]
+    N0 = Nb[fixed].sum(axis=0).reshape(n * d)
+    D0 = Db[fixed].sum(axis=0)
+    total = 2 ** free.size
+    for s0 in range(0, total, 2048):                         # subsets in chunks
+        ids = np.arange(s0, min(total, s0 + 2048))
+        masks = ((ids[:, None] >> np.arange(free.size)[None, :]) & 1).astype(np.float64)
+        prob = np.prod(np.where(masks > 0, pi[free][None, :], 1.0 - pi[free][None, :]), axis=1)
+        num = (N0[None] + masks @ Nf).reshape(-1, n, d)
+        den = D0[None] + masks @ Df
+        o = np.zeros_like(num)
+        nz = den > 0
+        o[nz] = num[nz] / den[nz][:, None]
+        m1 += np.einsum("s,snd->nd", prob, o)
+        m2 += np.einsum("s,snd->nd", prob, o * o)
+    return m1, m2

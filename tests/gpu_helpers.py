@@ -78,3 +78,35 @@ def sample_rows(NQ: int, BH: int, n: int, seed: int = 12345, tails: int = 4):
     for bh in rng.choice(BH, size=min(tails, BH), replace=False):
         rows.add(int(bh) * NQ + NQ - 1)  # the head's tail query block
     return sorted(rows)
+
+
+def assert_selection_bit_exact(absa, wl: Workload, C: int, Tk: int, mode: int, seed: int, stream_id: int = 3):
+    """absa_select on an integer workload (alpha 1, keep 25%) against the oracle: counts, indices,
+    weights and probabilities bit-identical, and the workspace's block means, centroids, cluster
+    sizes and scores equal to the oracle's intermediates."""
+    import torch
+    p = problem(wl)
+    lists, pi, ws = absa.select(p, dev(wl.q), dev(wl.k), 0.25, clusters=C, kmeans_steps=Tk,
+                                select_scale_log2=1.0, seed=seed, stream_id=stream_id, mode=mode, want_pi=True)
+    torch.cuda.synchronize()
+    count, kv, w = lists_to_host(lists)
+    res = O.select(wl.q, wl.k, wl.q_block, wl.kv_block, 0.25, C=C, Tk=Tk, alpha=1.0, seed=seed, stream=stream_id,
+                   mode=mode, keep_intermediates=True)
+    np.testing.assert_array_equal(count, res.count)
+    for r in range(p.rows):
+        np.testing.assert_array_equal(kv[r, :count[r]], res.kv_idx[r])
+        np.testing.assert_array_equal(w[r, :count[r]].view(np.uint32), res.inv_pi[r].view(np.uint32))
+    np.testing.assert_array_equal(pi.cpu().numpy().view(np.uint32), res.pi_hat.view(np.uint32))
+    offs = absa.workspace_layout(p, 0.25, C, Tk, mode)
+    wsn = ws.cpu().numpy()
+    BH, NK, d = wl.B * wl.H, p.nk, wl.d
+    NKp = -(-NK // 64) * 64
+    kbarT = wsn[offs[0]: offs[0] + BH * d * NKp * 4].view(np.float32).reshape(BH, d, NKp)
+    np.testing.assert_array_equal(kbarT[:, :, :NK].transpose(0, 2, 1), res.kbar.astype(np.float32))
+    mu = wsn[offs[1]: offs[1] + p.rows * C * d * 4].view(np.float32).reshape(p.rows, C, d)
+    np.testing.assert_array_equal(mu, res.mu.astype(np.float32))
+    nj = wsn[offs[2]: offs[2] + p.rows * C * 4].view(np.int32).reshape(p.rows, C)
+    np.testing.assert_array_equal(nj, res.counts)
+    s = wsn[offs[3]: offs[3] + p.rows * NK * 4].view(np.float32).reshape(p.rows, NK)
+    np.testing.assert_array_equal(s, res.scores.astype(np.float32))
+    return count, kv, w

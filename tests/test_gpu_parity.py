@@ -314,7 +314,7 @@ def test_wan13b_480p_full(absa):
     _check_selection_and_attend(absa, wl, 0.10, rows=rows, tag="Wan2.1-1.3B 480p (sampled rows)")
 
 
-@pytest.mark.parametrize("keep", [0.08, 0.11])
+@pytest.mark.parametrize("keep", [0.08, 0.095, 0.11])
 def test_wan14b_720p_full(absa, keep):
     wl = _wan14b()
     p = problem(wl)

@@ -435,3 +435,44 @@ def test_page_scale_budgets_sit_in_the_reported_skip_range():
     for cfg in (2, 3, 4):
         for keep in CONFIGS[cfg].keep:
             assert lo - 1e-9 <= keep <= hi + 1e-9, (cfg, keep)
+
+
+# ----------------------------------------------------------------------------- second integer workload
+
+def test_integer_family_guard_and_moving_kmeans_match_scipy():
+    """The second integer workload (tests/exact_family.py): every block passes the fp32
+    exactness guard; where the k-means still moves after its first step, the oracle's S2 equals
+    scipy's kmeans2 step for step (it is the same Lloyd rule), and the guard rejects a block
+    whose clustering mixes two families (a non-power-of-two normaliser)."""
+    import warnings
+    from exact_family import gen_exact_family
+    from scipy.cluster.vq import kmeans2
+    for C, Tk in ((2, 3), (4, 2), (8, 3)):
+        wl = gen_exact_family(5, C, Tk)
+        assert wl.extra["moved_blocks"] >= 8
+        kbar = O.kv_block_means(wl.k[0, 0], 16)
+        nk = np.full(64, 16.0)
+        moved_seen = 0
+        for i in range(16):
+            X = wl.q[0, 0, i * 64:(i + 1) * 64].astype(np.float64)
+            ok, moved = O.selection_fp32_exact(X, kbar, nk, C, Tk, 1.0, 16.0)
+            assert ok
+            mu, cnt, lab = O.ibcs_kmeans(X, C, Tk)
+            init = np.stack([X[(j * 64) // C] for j in range(C)])
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                mu_s, lab_s = kmeans2(X, init, iter=Tk, minit="matrix", missing="warn")
+            np.testing.assert_array_equal(mu, mu_s)
+            np.testing.assert_array_equal(lab, lab_s)
+            moved_seen += moved
+        assert moved_seen >= 1
+    # a block made of two families merged into one cluster is not exact
+    from workloads import exact_family_block
+    rng = np.random.default_rng(3)
+    kbar = O.kv_block_means(gen_exact_family(1, 1, 1).k[0, 0], 16)
+    rejected = 0
+    for _ in range(40):
+        X = exact_family_block(rng, families=2)
+        ok, _ = O.selection_fp32_exact(X, kbar, np.full(64, 16.0), 1, 1, 1.0, 16.0)
+        rejected += not ok
+    assert rejected >= 30

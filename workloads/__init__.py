@@ -11,6 +11,8 @@ from .synth import (  # noqa: F401
     bf16_round,
     gen_config,
     gen_exact,
+    exact_keys,
+    exact_family_block,
     gen_micro,
     gen_fourier_heads,
 )

@@ -39,6 +39,8 @@ __all__ = [
     "bf16_bits",
     "gen_config",
     "gen_exact",
+    "exact_keys",
+    "exact_family_block",
     "gen_micro",
     "gen_fourier_heads",
 ]
@@ -294,3 +296,63 @@ def gen_exact(seed: int = 0, H: int = 2, groups_collapse: bool = False) -> Workl
     return Workload(q=q, k=k, v=v, B=B, H=H, L=L, d=d, T=T, Hs=Hs, Ws=Ws, q_block=Bq, kv_block=Bk,
                     keep=0.25, name="exact-integer", extra={"clusters": 4, "kmeans_steps": 3,
                                                            "select_scale_log2": 1.0})
+
+
+def exact_keys(seed: int, H: int = 2, L: int = 1024, d: int = 64, Bk: int = 16) -> np.ndarray:
+    """Keys [1, H, L, d] whose KV block b (Bk keys) is e_b (one-hot at channel b) plus integer
+    perturbations in {-1, 0, 1} that sum to zero over the block, so its mean key is exactly e_b
+    (needs L / Bk == d)."""
+    assert L // Bk == d and L % Bk == 0
+    rng = np.random.default_rng([seed, 7779])
+    k = np.zeros((1, H, L, d), dtype=np.float32)
+    for h in range(H):
+        for b in range(L // Bk):
+            blk = np.zeros((Bk, d), dtype=np.float32)
+            for c in range(d):
+                j = int(rng.integers(0, Bk // 2 + 1))
+                idx = rng.permutation(Bk)[: 2 * j]
+                blk[idx[:j], c] = 1.0
+                blk[idx[j:], c] = -1.0
+            blk[:, b] += 1.0
+            k[0, h, b * Bk:(b + 1) * Bk] = blk
+    return k
+
+
+def exact_family_block(rng: np.random.Generator, d: int = 64, groups: int = 8, rows_per_group: int = 8,
+                       families: Optional[int] = None) -> np.ndarray:
+    """One candidate query block [groups * rows_per_group, d] of small integers for the second
+    integer workload: ``groups`` groups of identical rows, randomly interleaved.
+
+    The groups fall into ``families`` (1, 2 or 4; random if None) of equal size.  All groups of a
+    family share one active pattern: a multiset of exponents on random channels, made from {E}
+    (E ~ U{0..6}) by repeatedly splitting a term e into two terms e - 1 (depth <= 10), so that
+    sum 2^a is a power of two; the other channels hold -80 - 16 u with u in {0, 1} drawn per
+    group and channel, which separates the groups of a family.  Values are integers with
+    |x| <= 96, exact in bf16.  Whether a block's selection stays exactly representable depends
+    on how the clustering merges the groups, so callers keep only the blocks that pass such a
+    check.
+    """
+    if families is None:
+        families = int(rng.choice([1, 2, 4]))
+    assert groups % families == 0
+    per = groups // families
+    centres = []
+    for _f in range(families):
+        E = int(rng.integers(0, 7))
+        terms = [E]
+        for _ in range(int(rng.integers(0, 16))):
+            cand = [t for t in range(len(terms)) if terms[t] > E - 10]
+            if not cand:
+                break
+            t = cand[int(rng.integers(0, len(cand)))]
+            e = terms.pop(t)
+            terms += [e - 1, e - 1]
+        chans = rng.choice(d, size=len(terms), replace=False)
+        active = np.zeros(d, dtype=bool)
+        active[chans] = True
+        for _g in range(per):
+            c = (-80.0 - 16.0 * rng.integers(0, 2, size=d)).astype(np.float32)
+            c[chans] = np.asarray(terms, dtype=np.float32)
+            centres.append(c)
+    rows = np.repeat(np.stack(centres), rows_per_group, axis=0)
+    return rows[rng.permutation(rows.shape[0])]
