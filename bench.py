@@ -31,11 +31,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--keep", type=float, default=0.095)
+    ap.add_argument("--config", type=int, default=3, choices=(2, 3, 4),
+                    help="2: Wan2.1-1.3B-shaped 480p, 3: Wan2.1-14B-shaped 720p (default), "
+                         "4: HunyuanVideo-shaped 720p")
+    ap.add_argument("--keep", type=float, default=None, help="block budget (default: 9.5% for config 3, "
+                                                                  "else the workload's own)")
     ap.add_argument("--kv-block", type=int, default=16)
     ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1920)
+    ap.add_argument("--cpu-single-rows", type=int, default=240, help="rows of the one-thread oracle sample")
     ap.add_argument("--extra", action="store_true", help="also time the dense kernel, the FP8 variant and per-cluster lists")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the JSON line: accuracy and time of SIP / top-k / block-size / prior-art "
@@ -221,23 +226,14 @@ def measured_traffic(workload_tag="wan14b_720p"):
     return None
 
 
-def cpu_baseline(wl, keep, kv_block, nrows):
-    """fp64 oracle on a bounded sample: S1 for one head plus S2-S6 for ``nrows`` seeded rows,
-    extrapolated to the whole workload."""
+def _oracle_sample(wl, keep, kv_block, rows):
+    """Seconds the fp64 oracle takes for S1 of one head and for S2-S6 of ``rows``."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
-    Bq, d, L = wl.q_block, wl.d, wl.L
-    NQ, NK = O.num_blocks(L, Bq), O.num_blocks(L, kv_block)
-    BH = wl.B * wl.H
+    Bq, d = wl.q_block, wl.d
+    NQ = O.num_blocks(wl.L, Bq)
     sigma = 1.0 / math.sqrt(d)
     keep32 = float(np.float32(keep))
-    rng = np.random.default_rng(12345)
-    rows = sorted(int(r) for r in rng.choice(BH * NQ, size=nrows, replace=False))
     t0 = time.perf_counter()
     O.kv_block_means(wl.k[0, rows[0] // NQ], kv_block)
     t_s1 = time.perf_counter() - t0
@@ -249,14 +245,42 @@ def cpu_baseline(wl, keep, kv_block, nrows):
     # the per-row timing above includes S1 of each sampled head once; remove it
     heads = len(set(r // NQ for r in rows))
     per_row = max(t_rows - heads * t_s1, 1e-9) / len(rows)
+    return t_s1, t_rows, per_row
+
+
+def cpu_baseline(wl, keep, kv_block, nrows, nrows_single):
+    """fp64 oracle on a bounded sample: S1 for one head plus S2-S6 for ``nrows`` seeded rows,
+    extrapolated to the whole workload; then the same on ``nrows_single`` rows with one thread."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threadpool_limits = None
+        threads = len(os.sched_getaffinity(0))
+    NQ = O.num_blocks(wl.L, wl.q_block)
+    BH = wl.B * wl.H
+    dense_flops = 4.0 * wl.B * wl.H * float(wl.L) ** 2 * wl.d
+    rng = np.random.default_rng(12345)
+    rows = sorted(int(r) for r in rng.choice(BH * NQ, size=nrows, replace=False))
+    t_s1, t_rows, per_row = _oracle_sample(wl, keep, kv_block, rows)
     full_s = BH * t_s1 + BH * NQ * per_row
-    dense_flops = 4.0 * wl.B * wl.H * float(L) ** 2 * d
-    return {"value": dense_flops / full_s / 1e12, "unit": "dense-equivalent TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: KV block means of one head ({t_s1:.2f} s) and selection + "
-                       f"1/pi-weighted attention of {len(rows)} seeded rows ({t_rows:.2f} s) of the "
-                       f"same workload, extrapolated to {BH} heads x {NQ} query blocks "
-                       f"({full_s:.0f} s)")}
+    out = {"value": dense_flops / full_s / 1e12, "unit": "dense-equivalent TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "rows_per_s": 1.0 / per_row,
+           "sample": (f"fp64 NumPy oracle: KV block means of one head ({t_s1:.2f} s) and selection + "
+                      f"1/pi-weighted attention of {len(rows)} seeded rows ({t_rows:.2f} s) of the "
+                      f"same workload, extrapolated to {BH} heads x {NQ} query blocks "
+                      f"({full_s:.0f} s)")}
+    if threadpool_limits is not None and nrows_single > 0:
+        rows1 = rows[:nrows_single]
+        with threadpool_limits(limits=1):
+            t1_s1, t1_rows, per_row1 = _oracle_sample(wl, keep, kv_block, rows1)
+        full1 = BH * t1_s1 + BH * NQ * per_row1
+        out["single_thread"] = {"value": dense_flops / full1 / 1e12, "rows_per_s": 1.0 / per_row1, "cores": 1,
+                                "sample": f"the first {len(rows1)} of those rows on one thread ({t1_rows:.2f} s), "
+                                          f"extrapolated the same way ({full1:.0f} s)"}
+    return out
 
 
 def main():
@@ -274,9 +298,12 @@ def main():
     import block_sparse_attention_34_amd as absa
     from workloads import gen_config
 
+    from workloads import CONFIGS
     heads = list(range(args.heads)) if args.heads else None
+    if args.keep is None:
+        args.keep = 0.095 if args.config == 3 else CONFIGS[args.config].keep[0]
     t0 = time.perf_counter()
-    wl = gen_config(3, heads=heads, kv_block=args.kv_block)
+    wl = gen_config(args.config, heads=heads, kv_block=args.kv_block)
     print(f"[bench] generated {wl.name} H={wl.H} L={wl.L} in {time.perf_counter() - t0:.1f}s",
           file=sys.stderr, flush=True)
     p = absa.Problem(wl.B, wl.H, wl.L, wl.d, wl.T, wl.Hs, wl.Ws, wl.q_block, args.kv_block)
@@ -324,8 +351,11 @@ def main():
     nk_valid = torch.clamp(L - blk * Bk, max=Bk).double() * mask
     kept_keys = nk_valid.sum(dim=1)
     alg_flops = float((4.0 * nq_valid * d * kept_keys).sum())
+    # the attention kernel runs rows 2p and 2p + 1 together, max(T, T') 64-key steps each
     tiles = (count * Bk + 63) // 64
-    exec_flops = float((4.0 * Bq * 64 * d * tiles.double()).sum())
+    tp = torch.nn.functional.pad(tiles, (0, tiles.numel() % 2)).view(-1, 2)
+    exec_tiles = 2.0 * float(tp.max(dim=1).values.double().sum())
+    exec_flops = 4.0 * Bq * 64 * d * exec_tiles
     alg_bytes = float(kept_keys.sum()) * 4 * d  # K + V bf16 gathered per kept key
     dense_flops = 4.0 * p.B * p.H * float(L) ** 2 * d
     att_avg = sum(att_ms) / len(att_ms)
@@ -349,7 +379,7 @@ def main():
                    "selection": "IBCS + SIP", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic() if (Bk == 16 and p.H == 40 and
+                     "traffic": measured_traffic() if (args.config == 3 and Bk == 16 and p.H == 40 and
                                                        abs(args.keep - 0.095) < 1e-9) else None},
         "attend_ms": att_avg,
         "select_ms": sel_avg,
@@ -358,6 +388,18 @@ def main():
         "kept_fraction": float(count.double().mean()) / NK,
         "gather_GBs": alg_bytes / (att_avg * 1e-3) / 1e9,
     }
+    # accuracy of the timed step's output against dense attention, and of top-k lists of the same
+    # budget (after the timed region)
+    o_dense = torch.empty_like(o)
+    absa.dense(p, q, k, v, out=o_dense)
+    ref_norm = float(torch.linalg.vector_norm(o_dense))
+    o_tk = torch.empty_like(o)
+    lists_tk = absa.alloc_lists(p)
+    absa.select(p, q, k, args.keep, seed=0, mode="topk", lists=lists_tk, workspace=ws)
+    absa.attend(p, q, k, v, lists_tk, out=o_tk)
+    line["rel_l2_vs_dense"] = {"sip": float(torch.linalg.vector_norm(o - o_dense)) / ref_norm,
+                               "topk": float(torch.linalg.vector_norm(o_tk - o_dense)) / ref_norm}
+    del o_dense, o_tk, lists_tk
     if args.extra:
         for _ in range(2):
             absa.dense(p, q, k, v, out=o)
@@ -413,7 +455,8 @@ def main():
             line["clusters_union_fraction"] = float(cl.count.double().mean()) / p.nk
             del cl, cws, oc
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.keep, args.kv_block, args.cpu_sample_rows)
+        line["cpu_baseline"] = cpu_baseline(wl, args.keep, args.kv_block, args.cpu_sample_rows,
+                                            args.cpu_single_rows)
     print(json.dumps(line), flush=True)
 
 

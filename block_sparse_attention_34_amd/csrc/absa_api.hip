@@ -2,6 +2,7 @@
 // caller's stream.  Declarations and the contract are in include/absa.h.
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <mutex>
 
 #include "absa.h"
@@ -85,8 +86,13 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
+// Regions: kbar^T, centroids, cluster sizes, scores [lists][NKs] (NKs = NK
+// rounded up to 4; one list per row, or per (row, cluster) for per-cluster
+// lists), the logit slot (SIZE_MAX: logits are never stored), per-split (max,
+// normaliser), the block means' bf16 halves in operand order.
+WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C, int lists_per_row) {
   WsLayout w;
+  const size_t NKs = (size_t)((dm.NK + 3) & ~3);
   size_t o = 0;
   w.off[0] = o;
   o = align_up(o + (size_t)dm.BH * p->d * dm.NKp * sizeof(float), kWsAlign);
@@ -95,9 +101,8 @@ WsLayout ws_layout(const absa_problem* p, const Dims& dm, int C) {
   w.off[2] = o;
   o = align_up(o + (size_t)dm.rows * C * sizeof(int32_t), kWsAlign);
   w.off[3] = o;
-  o = align_up(o + (size_t)dm.rows * dm.NK * sizeof(float), kWsAlign);
-  w.off[4] = o;
-  o = align_up(o + (size_t)dm.rows * C * dm.NKp * sizeof(float), kWsAlign);
+  o = align_up(o + (size_t)dm.rows * lists_per_row * NKs * sizeof(float), kWsAlign);
+  w.off[4] = SIZE_MAX;
   w.off[5] = o;
   int per;
   const int nsplit = absa::logit_splits(dm.NQ, C, (int)dm.BH, dm.NKp, &per);
@@ -117,11 +122,8 @@ struct WsClusters {
 
 WsClusters ws_layout_clusters(const absa_problem* p, const Dims& dm, int C) {
   WsClusters w;
-  w.base = ws_layout(p, dm, C);
+  w.base = ws_layout(p, dm, C, C);
   size_t o = w.base.total;
-  // the score region (offset 3) grows from [rows][NK] to [rows * C][NK]: give it a new home at the end
-  w.base.off[3] = o;
-  o = align_up(o + (size_t)dm.rows * C * dm.NK * sizeof(float), kWsAlign);
   w.ccount = o;
   o = align_up(o + (size_t)dm.rows * C * sizeof(int32_t), kWsAlign);
   w.cidx = o;
@@ -251,7 +253,7 @@ absa_status absa_select_workspace(const absa_problem* prob, const absa_select_pa
   if (st != ABSA_OK) return st;
   st = check_params(prob, params, &sp);
   if (st != ABSA_OK) return st;
-  *bytes = ws_layout(prob, dm, sp.C).total;
+  *bytes = ws_layout(prob, dm, sp.C, 1).total;
   return ABSA_OK;
 }
 
@@ -264,7 +266,7 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
   if (st != ABSA_OK) return st;
   st = check_params(prob, params, &sp);
   if (st != ABSA_OK) return st;
-  const WsLayout w = ws_layout(prob, dm, sp.C);
+  const WsLayout w = ws_layout(prob, dm, sp.C, 1);
   for (int i = 0; i < 5; ++i) offsets[i] = w.off[i];
   return ABSA_OK;
 }
@@ -299,7 +301,6 @@ static absa::SelectLaunch select_launch(const absa_problem* prob, const absa_sel
   a.mu = reinterpret_cast<float*>(ws + w.off[1]);
   a.nj = reinterpret_cast<int*>(ws + w.off[2]);
   a.s = reinterpret_cast<float*>(ws + w.off[3]);
-  a.logit = reinterpret_cast<float*>(ws + w.off[4]);
   a.mz = reinterpret_cast<float2*>(ws + w.off[5]);
   a.kbh = reinterpret_cast<uint16_t*>(ws + w.off[6]);
   return a;
@@ -320,7 +321,7 @@ static absa_status check_select(const absa_problem* prob, const absa_select_para
   st = check_lists(out, true, dm->NK);
   if (st != ABSA_OK) return st;
   if (pi_out && !aligned(pi_out, 4)) return ABSA_ERR_ALIGNMENT;
-  *w = ws_layout(prob, *dm, sp->C);
+  *w = ws_layout(prob, *dm, sp->C, 1);
   return ABSA_OK;
 }
 
@@ -336,6 +337,7 @@ static absa_status run_select(const absa_problem* prob, const absa_select_params
   a.inv_pi = out->inv_pi;
   a.cap = out->cap;
   a.pi_out = pi_out;
+  if (!pi_out) a.kbarT = nullptr;  // the fp32 block means are stored only for inspection
   hipError_t e = absa::launch_select(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
@@ -403,6 +405,7 @@ absa_status absa_select_clusters(const absa_problem* prob, const absa_select_par
   char* ws = static_cast<char*>(workspace);
   absa::SelectLaunch a = select_launch(prob, params, dm, sp, w.base, ws, q, k);
   a.per_cluster = 1;
+  a.kbarT = nullptr;
   a.count = reinterpret_cast<int32_t*>(ws + w.ccount);
   a.kv_idx = reinterpret_cast<int32_t*>(ws + w.cidx);
   a.inv_pi = reinterpret_cast<float*>(ws + w.cw);

@@ -24,6 +24,18 @@ __device__ __forceinline__ void unpack_bf16x2(uint32_t w, float& lo, float& hi) 
   hi = __uint_as_float(w & 0xFFFF0000u);
 }
 
+// ----------------------------------------------------------------------------- scalar pointers
+// A wave-uniform pointer rebuilt from the first lane's two 32-bit halves, for
+// buffer resources (which live in scalar registers).  The halves are taken as
+// unsigned: readfirstlane returns int, and a sign-extended low half would fill
+// the high half with ones whenever bit 31 of the address is set.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32))));
+  return reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // ----------------------------------------------------------------------------- Philox4x32-10
 // One round: the two 32x32->64 products of words 0 and 2 with the round
 // multipliers feed a xor with words 1/3 and the round key; the key advances by

@@ -12,12 +12,11 @@ struct SelectLaunch {
   int B, H, L, d, Bq, Bk, NQ, NK, NKp, C, Tk, mode, kstar, cap;
   float nstar, alpha;
   uint32_t key0, key1, ctr3;
-  float* kbarT;  // workspace: [BH][d][NKp]
-  uint16_t* kbh; // workspace: [2][BH][NKp][d] bf16 head, then tail, of the block means
+  float* kbarT;  // workspace: [BH][d][NKp], written only when not null
+  uint16_t* kbh; // workspace: block means' bf16 heads and tails in matrix operand order
   float* mu;     // workspace: [rows][C][d]
   int* nj;       // workspace: [rows][C]
-  float* s;      // workspace: [rows][NK]
-  float* logit;  // workspace: [rows][C][NK]
+  float* s;      // workspace: scores [lists][NK rounded up to 4]
   float2* mz;    // workspace: [rows][C][nsplit] per-split (max, normaliser) of each centroid
   int32_t* count;
   int32_t* kv_idx;

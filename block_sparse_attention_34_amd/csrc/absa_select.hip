@@ -21,10 +21,14 @@ namespace absa {
 __device__ __forceinline__ float exp2_split(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================================================================= K1
-// kbar^T[bh][c][b] = (1/n_b) sum_{valid keys of block b} K[bh][key][c], and the
-// same means block-major as bf16 head and tail, hi = bf16(kbar), lo =
-// bf16(kbar - hi) (kbh[bh][b][c], then kbl at kbh + BH NKp D), the operands of
-// the logit product.  Padding blocks (b >= NK) are 0.
+// kbar^T[bh][c][b] = (1/n_b) sum_{valid keys of block b} K[bh][key][c] (written
+// only when kbarT is not null), and the same means as bf16 head and tail, hi =
+// bf16(kbar), lo = bf16(kbar - hi), the B operands of the logit product, in
+// the matrix core's operand order: for each 32-block tile T and k-step s the
+// 64 lanes' 16-byte operands lie contiguously, heads then tails,
+// kbh[bh][T][s][hl][lane][8], lane (h, n) holding block 32 T + n, channels
+// 16 s + 8 h .. + 7, so a wave reads each operand as one 1 KB piece.  Padding
+// blocks (b >= NK) are 0.
 // Grid (NKp/64, BH), 256 threads; a workgroup produces 64 blocks x D dims.
 template <int D>
 __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __restrict__ k,
@@ -76,25 +80,27 @@ __global__ __launch_bounds__(256) void kv_block_mean_kernel(const uint16_t* __re
     for (int e = 0; e < 8; ++e) tile[c * 8 + e][bl] = acc[e];
   }
   __syncthreads();
-  float* dst = kbarT + (size_t)bh * D * NKp + b0;
-  for (int idx = t; idx < D * 64; idx += 256) {
-    const int cc = idx >> 6, bl = idx & 63;
-    dst[(size_t)cc * NKp + bl] = tile[cc][bl];
+  if (kbarT) {
+    float* dst = kbarT + (size_t)bh * D * NKp + b0;
+    for (int idx = t; idx < D * 64; idx += 256) {
+      const int cc = idx >> 6, bl = idx & 63;
+      dst[(size_t)cc * NKp + bl] = tile[cc][bl];
+    }
   }
-  const size_t tail = (size_t)gridDim.y * NKp * D;
-  for (int idx = t; idx < 64 * D / 8; idx += 256) {
-    const int bl = idx / (D / 8), c8 = idx % (D / 8);
-    bf16x8 hv, lv;
+  // pieces (tile tt of the two here, k-step s, half hl, lane), 16 bytes each
+  constexpr int KS = D / 16;
+  for (int idx = t; idx < 2 * KS * 2 * 64; idx += 256) {
+    const int ln = idx & 63, hl = (idx >> 6) & 1, ks = (idx >> 7) % KS, tt = (idx >> 7) / KS;
+    const int bl = 32 * tt + (ln & 31), c0 = 16 * ks + 8 * (ln >> 5);
+    bf16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = tile[c8 * 8 + e][bl];
+      const float x = tile[c0 + e][bl];
       const __bf16 hi = (__bf16)x;
-      hv[e] = hi;
-      lv[e] = (__bf16)(x - (float)hi);
+      v[e] = hl ? (__bf16)(x - (float)hi) : hi;
     }
-    const size_t o = ((size_t)bh * NKp + b0 + bl) * D + c8 * 8;
-    *reinterpret_cast<bf16x8*>(kbh + o) = hv;
-    *reinterpret_cast<bf16x8*>(kbh + tail + o) = lv;
+    const size_t T = (size_t)bh * (NKp / 32) + (b0 / 32) + tt;
+    *reinterpret_cast<bf16x8*>(kbh + (((T * KS + ks) * 2 + hl) * 64 + ln) * 8) = v;
   }
 }
 
@@ -286,38 +292,82 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
 // head against every KV block: a [NQ*C x d] x [d x NK] product on the bf16
 // matrix core.  Each fp32 operand x is split into a bf16 head and tail,
 // x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) and |r| <= 2^-17 |x|,
-// and mu . kbar is formed as hi.hi' + hi.lo' + lo.hi' in one fp32 accumulator:
-// the dropped lo.lo' and remainder terms are below 2^-15 of each product, and
-// operands that bf16 holds exactly (lo = 0) give the exact fp32 dot product.
+// and mu . kbar is formed as hi.hi' + hi.lo' + lo.hi' in one fp32 accumulator
+// (per k-step, in that order): the dropped lo.lo' and remainder terms are
+// below 2^-15 of each product, and operands that bf16 holds exactly (lo = 0)
+// give the exact fp32 dot product.  The logits are formed twice and never
+// stored: once for the normalisers, once for the scores.
 // Workgroup = 4 waves x 32 centroids; a wave keeps its centroids' heads and
-// tails as A operands in registers and streams 32-block tiles of the means'
-// heads and tails (split once, by K1) through LDS.  Logit rows have NKp
-// entries (the padding holds -inf and is never read); a wave turns its 32 x 32
-// logits around in LDS so that each lane stores 16 contiguous bytes.
+// tails as A operands in registers.  The means' heads and tails (split once,
+// by K1, in operand order) pass through LDS one 32-block tile at a time, as a
+// copy of the tile's bytes: every wave then reads its B operands as
+// consecutive 16-byte pieces (no bank conflicts), and the global loads of a
+// tile are issued two tiles ahead of its store into LDS.
+// What a workgroup leaves depends on MODE:
+//  * LG_MZ: per centroid, the running max m and normaliser
+//    Z = sum nk 2^(l - m) over the split's blocks (terms more than 64 octaves
+//    below the max dropped), combined over the lanes in a fixed order;
+//  * LG_SCORE: with the max and normaliser of every centroid final (the
+//    LG_MZ splits combined in split order), the mixture score of every row of
+//    the wave's centroids and every block of the split,
+//      s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j        (j in order),
+//    into s[row][NKs];
+//  * LG_SCORE_PC: per-cluster lists: each cluster's own score
+//      s_jb = nk_b 2^(l_jb - m_j) / Z_j  into s[row C + j][NKs].
+// Score rows have NKs = NK rounded up to 4 entries, the tail set to 0.
 // Grid (ceil(M/128), BH, nsplit): split z covers a contiguous range of 32-block
 // tiles.
-template <int D>
-__global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restrict__ kbh,
-                                                         const float* __restrict__ mu,
-                                                         float* __restrict__ logit,
-                                                         float2* __restrict__ mz, int M, int NK,
-                                                         int NKp, int L, int Bk, int tiles_per_split,
-                                                         float alpha) {
-  constexpr int KS = D / 16;  // k-steps of 16 dims
-  // [buffer][block row][D] bf16, 16-byte chunks swizzled by row as in the
-  // attention kernels' K tiles, so the 32 rows a k-step reads are conflict-free
-  __shared__ __attribute__((aligned(16))) unsigned char khi[2][32 * D * 2], klo[2][32 * D * 2];
-  constexpr int LPS = 40;  // row stride of a wave's logit patch (the two half-waves' writes hit disjoint banks)
-  __shared__ __attribute__((aligned(16))) float lpatch[4][32 * LPS];
+constexpr int LG_MZ = 0, LG_SCORE = 1, LG_SCORE_PC = 2;
+
+template <int D, int MODE, int C>
+__global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __restrict__ kbh,
+                                                            const float* __restrict__ mu,
+                                                            float2* __restrict__ mz,
+                                                            const int* __restrict__ nj,
+                                                            float* __restrict__ s_out, int M, int NK, int NKs,
+                                                            int NKp, int L, int Bq, int Bk, int nsplit,
+                                                            int tiles_per_split, float alpha) {
+  constexpr int KS = D / 16;          // k-steps of 16 dims
+  constexpr int TB = KS * 2048;       // bytes of one tile's operands (heads and tails)
+  constexpr int NST = TB / (256 * 16);  // 16-byte pieces per thread and tile
+  constexpr bool SCORE = MODE != LG_MZ;
+  __shared__ __attribute__((aligned(16))) unsigned char kt[2][TB];
+  __shared__ float mj_s[SCORE ? 128 : 1], coef_s[SCORE ? 128 : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) index
   const int h = lane >> 5, n = lane & 31;
   const int bh = blockIdx.y;
   const int m0 = blockIdx.x * 128 + w * 32;
+  const int NT = NKp / 32;
   const int tile0 = blockIdx.z * tiles_per_split;
-  const int ntile_all = NKp / 32;
-  const int tile1 = min(ntile_all, tile0 + tiles_per_split);
-  if (tile0 >= tile1) return;
+  const int tile1 = min(NT, tile0 + tiles_per_split);
+  const bool active = m0 < M;  // waves without centroids still stage tiles
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(kbh) + (size_t)bh * NT * TB;
+
+  if constexpr (SCORE) {
+    // max, normaliser and score coefficient of the workgroup's 128 centroids:
+    // (n_j/n)/Z_j for the mixture, 1/Z_j for a cluster's own score
+    if (t < 128) {
+      const int m = blockIdx.x * 128 + t;
+      float mx = -INFINITY, coef = 0.f;
+      if (m < M) {
+        const float2* pz = mz + ((size_t)bh * M + m) * nsplit;
+        for (int z = 0; z < nsplit; ++z) mx = fmaxf(mx, pz[z].x);
+        float zs = 0.f;
+        for (int z = 0; z < nsplit; ++z) {
+          const float d = pz[z].x - mx;
+          if (d >= -64.f) zs = fmaf(pz[z].y, exp2_split(d), zs);
+        }
+        const int i = m / C;
+        const int nq = min(Bq, L - i * Bq);
+        const int cnt = nj[(size_t)bh * M + m];
+        if (MODE == LG_SCORE) coef = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)nq), zs) : 0.f;
+        else coef = __fdiv_rn(1.f, zs);
+      }
+      mj_s[t] = mx;
+      coef_s[t] = coef;
+    }
+  }
 
   // A operands: lane (h, n) holds mu[m0 + n][16 s + 8 h + e], e = 0..7, as head and tail
   bf16x8 ahi[KS], alo[KS];
@@ -338,98 +388,124 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
         }
       }
   }
-  // 16-byte chunks of a tile: NCK per operand (head, tail), NST per thread
-  constexpr int NCK = 32 * D / 8, NST = 2 * NCK / 256;
-  const uint16_t* kb = kbh + (size_t)bh * NKp * D;
-  const size_t tail = (size_t)gridDim.y * NKp * D;
-  // two register stages: the global loads of a tile are issued two tiles
-  // ahead of its store into LDS, so their latency spans two tile periods
-  u32x4 stA[NST], stB[NST];
   auto fetch = [&](u32x4 (&stage)[NST], int tile) {
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int idx = t + 256 * i, rem = idx % NCK;
-      stage[i] = *reinterpret_cast<const u32x4*>(kb + (idx >= NCK ? tail : 0) + (size_t)(tile * 32) * D + rem * 8);
-    }
+    for (int i = 0; i < NST; ++i)
+      stage[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)tile * TB + (t + 256 * i) * 16);
   };
   auto put = [&](const u32x4 (&stage)[NST], int buf) {
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int idx = t + 256 * i, rem = idx % NCK;
-      const int off = k_off<D>(rem / (D / 8), rem % (D / 8));
-      *reinterpret_cast<u32x4*>(idx >= NCK ? &klo[buf][off] : &khi[buf][off]) = stage[i];
-    }
+    for (int i = 0; i < NST; ++i) *reinterpret_cast<u32x4*>(&kt[buf][(t + 256 * i) * 16]) = stage[i];
   };
+  u32x4 stA[NST], stB[NST];
   fetch(stA, tile0);
   put(stA, 0);
   if (tile0 + 1 < tile1) fetch(stA, tile0 + 1);
-  // this wave's output window: logit rows m0 .. m0+31 (those below M) of the head
-  const int rows_here = max(0, min(32, M - m0));
-  const uint64_t obase = (uint64_t)(logit + ((size_t)bh * M + (rows_here > 0 ? m0 : 0)) * NKp);
-  const uint32_t obase_lo = __builtin_amdgcn_readfirstlane((uint32_t)obase);
-  const uint32_t obase_hi = __builtin_amdgcn_readfirstlane((uint32_t)(obase >> 32));
-  const int obytes = __builtin_amdgcn_readfirstlane(rows_here * NKp * 4);
-  float* const lp = lpatch[w];
-  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(((uint64_t)obase_hi << 32) | obase_lo), 0, obytes, 0x00020000);
-  // running max m and normaliser Z = sum nk 2^(l - m) of the 16 centroids this
-  // lane sees (terms more than 64 octaves below the max dropped)
-  float rm[16], rz[16];
+
+  const int rows_here = max(0, min(32, M - m0));  // the wave's centroids below M
+  float rm[16], rz[16];  // LG_MZ: running max and normaliser of the lane's 16 centroids
+  float mj[16], cf[16];  // scores: final max and coefficient of the lane's 16 centroids
 #pragma unroll
-  for (int r = 0; r < 16; ++r) { rm[r] = -INFINITY; rz[r] = 0.f; }
-  // one tile: sput holds tile + 1 (stored into the other LDS buffer at the
-  // end), sfetch receives tile + 2; the loop alternates the two stages
+  for (int r = 0; r < 16; ++r) { rm[r] = -INFINITY; rz[r] = 0.f; mj[r] = 0.f; cf[r] = 0.f; }
+  if constexpr (SCORE) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = w * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      mj[r] = mj_s[m];
+      cf[r] = coef_s[m];
+    }
+  }
+  // LG_SCORE: first score row of the wave's centroids (rows m0/C ..); LG_SCORE_PC: row of centroid m0
+  float* const srow = (MODE == LG_SCORE) ? s_out + ((size_t)bh * (M / C) + m0 / C) * NKs
+                                         : s_out + ((size_t)bh * M + m0) * NKs;
+  const int nrows_w = (MODE == LG_SCORE) ? rows_here / C : rows_here;
+
   auto body = [&](int tile, const u32x4 (&sput)[NST], u32x4 (&sfetch)[NST]) {
     const int buf = (tile - tile0) & 1;
     __syncthreads();
     if (tile + 2 < tile1) fetch(sfetch, tile + 2);
-    // B operands: lane (h, n) reads block n, channels 16 s + 8 h .. +7
-    f32x16 acc;
+    if (active) {
+      const unsigned char* kl = &kt[buf][lane * 16];
+      f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    // operand reads two k-steps ahead of their products (fewer live registers)
-    bf16x8 bhi[KS], blo[KS];
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const int off = k_off<D>(n, 2 * s2 + h);
-      bhi[s2] = *reinterpret_cast<const bf16x8*>(&khi[buf][off]);
-      blo[s2] = *reinterpret_cast<const bf16x8*>(&klo[buf][off]);
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(kl + ks * 2048);
+        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(kl + ks * 2048 + 1024);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], blo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], bhi, acc, 0, 0, 0);
+      }
+      const int b = tile * 32 + n;
+      const bool bv = b < NK;
+      const float nk = (float)min(Bk, L - b * Bk);
+      if constexpr (SCORE) {
+        // lane (h, n) register r: centroid m0 + 8 (r/4) + 4 h + r%4 against block b
+        float term[16];
+        uint32_t ok = 0u;
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s2], bhi[s2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[s2], blo[s2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[s2], bhi[s2], acc, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int r = 0; r < 16; ++r) {
+          const float dl = alpha * acc[r] - mj[r];
+          const bool on = dl >= -64.f && cf[r] != 0.f;
+          term[r] = on ? nk * exp2_split(dl) : 0.f;
+          ok |= on ? (1u << r) : 0u;
+        }
+        if constexpr (MODE == LG_SCORE_PC) {
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      if (s2 + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
-    // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
-    // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z; stores
-    // of rows >= M fall outside the window and are dropped.
-    const int b = tile * 32 + n;
-    const bool bv = b < NK;
-    const float nk = (float)min(Bk, L - b * Bk);
+          for (int r = 0; r < 16; ++r) {
+            const int rl = 8 * (r >> 2) + 4 * h + (r & 3);
+            const float sv = ((ok >> r) & 1u) ? fmaf(cf[r], term[r], 0.f) : 0.f;
+            if (b < NKs && rl < nrows_w) srow[(size_t)rl * NKs + b] = bv ? sv : 0.f;
+          }
+        } else if constexpr (C <= 4) {
+          // the C centroids of a row are consecutive registers of one lane
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float l = bv ? alpha * acc[r] : -INFINITY;
-      lp[(8 * (r >> 2) + 4 * h + (r & 3)) * LPS + n] = l;
-      const float dd = fabsf(rm[r] - l);
-      const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
-      const bool up = l > rm[r];
-      rz[r] = fmaf(rz[r], up ? e : 1.f, up ? nk : nk * e);
-      rm[r] = up ? l : rm[r];
-    }
-    // lane i stores blocks 4 (i % 8) .. +3 of patch rows 8 q + i / 8
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int pr = 8 * q + (lane >> 3), c4 = 4 * (lane & 7);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&lp[pr * LPS + c4]);
-      __builtin_amdgcn_raw_buffer_store_b128(v, ors, (pr * NKp + tile * 32 + c4) * 4, 0, 0);
+            for (int gg = 0; gg < 4 / C; ++gg) {
+              float sv = 0.f;
+#pragma unroll
+              for (int j = 0; j < C; ++j) {
+                const int r = 4 * q + gg * C + j;
+                if ((ok >> r) & 1u) sv = fmaf(cf[r], term[r], sv);
+              }
+              const int rl = (8 * q + 4 * h + gg * C) / C;
+              if (b < NKs && rl < nrows_w) srow[(size_t)rl * NKs + b] = bv ? sv : 0.f;
+            }
+        } else {
+          // C = 8: row q's centroids 0..3 sit in half-wave 0 (registers 4 q ..),
+          // 4..7 in half-wave 1; half 1 continues the sum half 0 started
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float sv = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (h == 0 && ((ok >> (4 * q + j)) & 1u)) sv = fmaf(cf[4 * q + j], term[4 * q + j], sv);
+            sv = __shfl_xor(sv, 32, 64);
+            if (h == 1) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if ((ok >> (4 * q + j)) & 1u) sv = fmaf(cf[4 * q + j], term[4 * q + j], sv);
+              if (b < NKs && q < nrows_w) srow[(size_t)q * NKs + b] = bv ? sv : 0.f;
+            }
+          }
+        }
+      } else {
+        // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
+        // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
+        // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float l = bv ? alpha * acc[r] : -INFINITY;
+          const float dd = fabsf(rm[r] - l);
+          const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
+          const bool up = l > rm[r];
+          rz[r] = fmaf(rz[r], up ? e : 1.f, up ? nk : nk * e);
+          rm[r] = up ? l : rm[r];
+        }
+      }
     }
     if (tile + 1 < tile1) put(sput, buf ^ 1);
   };
@@ -438,266 +514,263 @@ __global__ __launch_bounds__(256) void ibcs_logit_kernel(const uint16_t* __restr
     body(tile, stA, stB);
     if (tile + 1 < tile1) body(tile + 1, stB, stA);
   }
-  // combine over the 32 blocks (lanes) of each half-wave and write this split's
-  // partial (m, Z) of every centroid
+  if constexpr (!SCORE) {
+    if (!active) return;
+    // combine over the 32 blocks (lanes) of each half-wave and write this split's
+    // partial (m, Z) of every centroid
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; ++r) {
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      const float m2 = __shfl_xor(rm[r], o, 64), z2 = __shfl_xor(rz[r], o, 64);
-      const float mn = fmaxf(rm[r], m2);
-      const float d0 = rm[r] - mn, d1 = m2 - mn;
-      const float e0 = d0 >= -64.f ? exp2_split(d0) : 0.f;
-      const float e1 = d1 >= -64.f ? exp2_split(d1) : 0.f;
-      rz[r] = fmaf(rz[r], e0, z2 * e1);
-      rm[r] = mn;
+      for (int o = 1; o < 32; o <<= 1) {
+        const float m2 = __shfl_xor(rm[r], o, 64), z2 = __shfl_xor(rz[r], o, 64);
+        const float mn = fmaxf(rm[r], m2);
+        const float d0 = rm[r] - mn, d1 = m2 - mn;
+        const float e0 = d0 >= -64.f ? exp2_split(d0) : 0.f;
+        const float e1 = d1 >= -64.f ? exp2_split(d1) : 0.f;
+        rz[r] = fmaf(rz[r], e0, z2 * e1);
+        rm[r] = mn;
+      }
+      const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (n == 0 && m < M) mz[((size_t)bh * M + m) * nsplit + blockIdx.z] = make_float2(rm[r], rz[r]);
     }
-    const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (n == 0 && m < M) mz[((size_t)bh * M + m) * gridDim.z + blockIdx.z] = make_float2(rm[r], rz[r]);
   }
 }
 
 // ============================================================================= K3
-// One workgroup per row: inclusion probabilities by iterative capping, Philox
-// Bernoulli draws (or top-k / all), and compaction into the row's list.
-constexpr int SIP_NT = 256;
+// Sampling, one list per wave: the row's list (one list per row) or the list
+// of cluster j of a row (per-cluster lists: list row C + j, the full budget,
+// Philox counter word i C + j; a cluster without members gets an empty list).
+// Lane l holds the scores of four chunks of P contiguous blocks, those of the
+// threads l, l + 64, l + 128, l + 192 of a 256-thread layout that gives each
+// thread P blocks, in registers for the whole list:
+//  * SIP capping rounds in straight-line code.  A block is free while its
+//    register holds a positive score; capping sets it to -0, which adds
+//    nothing to a sum, is never capped again and stays apart from a zero
+//    score.  Every sum is taken in the layout's thread order (per-thread
+//    partials in block order, wave totals, the four wave totals in order);
+//  * top-k: the threshold bit pattern by bisection on the same registers,
+//    then the lowest-index ties;
+//  * the decisions: probability (1 capped, s R / S_U other positive scores, 0
+//    else), one Philox block per 4 consecutive blocks, and the list entries
+//    in block order (thread-order prefix sums).
+// No LDS and no workgroup barrier: each wave owns its list.
+constexpr int SR_WAVES = 4;  // lists per workgroup
 
-// Capping rounds of the SIP inclusion probabilities over one thread's chunk of
-// n <= PM block scores s[b0 .. b0+n).  The chunk stays in registers; each round
-// caps the free blocks with s R >= S_U and, in the same block reduction, forms
-// the sum over the blocks still free, which is the next round's S_U (the same
-// set, summed in the same order, as a fresh sum over the free blocks).  On
-// return flag[] holds 1 for capped, 0 for free (s > 0), 2 for zero blocks, and
-// R, S_U the remaining budget and free-score sum of the last round.
-template <int PM>
-__device__ __forceinline__ void sip_capping(const float* s, int b0, int n, float& R, float& S_U, unsigned char* flag,
-                                            float* redf, int* redi) {
-  float sv[PM];
-  uint64_t freem = 0ull, capm = 0ull;
-  float part = 0.f;
-  int nfree = 0;
-#pragma unroll
-  for (int e = 0; e < PM; ++e) {
-    sv[e] = (e < n) ? s[b0 + e] : 0.f;
-    if (sv[e] > 0.f) {
-      freem |= 1ull << e;
-      part += sv[e];
-      ++nfree;
-    }
-  }
-  int parity = 0;
-  block_total2<SIP_NT>(part, nfree, redf, redi, parity);
-  S_U = part;
-#pragma unroll 1
-  while (nfree > 0) {
-    int ncap = 0;
-    part = 0.f;
-#pragma unroll
-    for (int e = 0; e < PM; ++e) {
-      if ((freem >> e) & 1ull) {
-        if (__fmul_rn(sv[e], R) >= S_U) {
-          freem &= ~(1ull << e);
-          capm |= 1ull << e;
-          ++ncap;
-        } else {
-          part += sv[e];
-        }
-      }
-    }
-    parity ^= 1;
-    block_total2<SIP_NT>(part, ncap, redf, redi, parity);
-    if (ncap == 0) break;
-    S_U = part;
-    R -= (float)ncap;
-    nfree -= ncap;
-  }
-#pragma unroll
-  for (int e = 0; e < PM; ++e)
-    if (e < n) flag[b0 + e] = ((capm >> e) & 1ull) ? 1 : (sv[e] > 0.f ? 0 : 2);
-}
+__device__ __forceinline__ bool is_neg_zero(float x) { return __float_as_uint(x) == 0x80000000u; }
 
-template <int C>
-__global__ __launch_bounds__(SIP_NT) void sip_kernel(const float* __restrict__ logit,
-                                                     const float2* __restrict__ mz, int nsplit,
-                                                     const int* __restrict__ nj,
-                                                     float* __restrict__ s_out, int L, int Bq, int Bk,
-                                                     int NK, int NKp, int NQ,
-                                                     float nstar, int kstar, int mode, uint32_t key0,
-                                                     uint32_t key1, uint32_t ctr3,
-                                                     int32_t* __restrict__ count_out,
-                                                     int32_t* __restrict__ kv_idx,
-                                                     float* __restrict__ inv_pi, int cap,
-                                                     float* __restrict__ pi_out, int per_cluster) {
-  extern __shared__ float s[];                      // [NK]
-  unsigned char* flag = reinterpret_cast<unsigned char*>(s + NK);  // [NK]
-  __shared__ float redf[2 * (SIP_NT / 64)];
-  __shared__ int redi[2 * (SIP_NT / 64)];
-  const int t = threadIdx.x;
-  const int row = blockIdx.x;
-  const int bh = row / NQ, i = row % NQ;
-  // Per-cluster lists: workgroup (row, j) samples cluster j alone (its own block
-  // distribution, the full budget, Philox counter word i C + j) into list row C + j;
-  // a cluster without members gets an empty list.
-  const int jsel = per_cluster ? (int)blockIdx.y : -1;
-  const int orow = per_cluster ? row * C + jsel : row;
-  if (per_cluster && nj[(size_t)row * C + jsel] == 0) {
-    if (t == 0) count_out[orow] = 0;
+constexpr int SR_SIP = 0, SR_TOPK = 1;
+
+template <int PM, int MODE>
+__global__ __launch_bounds__(64 * SR_WAVES) void sip_rows_kernel(SelectLaunch a, int nlists, int NKs) {
+  const int lane = threadIdx.x & 63;
+  const int lst = blockIdx.x * SR_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lst >= nlists) return;
+  const int C = a.C;
+  const int row = a.per_cluster ? lst / C : lst;
+  const int jc = a.per_cluster ? lst - row * C : 0;
+  const int bh = row / a.NQ, i = row - bh * a.NQ;
+  const int NK = a.NK;
+  if (a.per_cluster && a.nj[(size_t)row * C + jc] == 0) {
+    if (lane == 0) a.count[lst] = 0;
     return;
   }
-
-  // ---- IBCS scores of this row from its logits: per centroid the max m_j and
-  // the normaliser Z_j = sum_b nk_b 2^(l_jb - m_j) (terms below 2^-64 of the
-  // max dropped; combined from the logit kernel's per-split partials), then
-  // s_b = sum_j (n_j/n) nk_b 2^(l_jb - m_j) / Z_j.
-  {
-    const float* lrow = logit + (size_t)row * C * NKp;
-    __shared__ float coef_s[C], mj_s[C];
-    if (t < C) {
-      const float2* pz = mz + ((size_t)row * C + t) * nsplit;
-      float m = -INFINITY;
-      for (int z = 0; z < nsplit; ++z) m = fmaxf(m, pz[z].x);
-      float zs = 0.f;
-      for (int z = 0; z < nsplit; ++z) {
-        const float d = pz[z].x - m;
-        if (d >= -64.f) zs = fmaf(pz[z].y, exp2_split(d), zs);
-      }
-      const int n = min(Bq, L - i * Bq);
-      const int cnt = nj[(size_t)row * C + t];
-      mj_s[t] = m;
-      if (per_cluster)
-        coef_s[t] = (t == jsel) ? __fdiv_rn(1.f, zs) : 0.f;
-      else
-        coef_s[t] = (cnt > 0) ? __fdiv_rn(__fdiv_rn((float)cnt, (float)n), zs) : 0.f;
-    }
-    __syncthreads();
-    float mj[C], coef[C];
+  const uint32_t ctr1 = a.per_cluster ? (uint32_t)(i * C + jc) : (uint32_t)i;
+  const int P = ((NK + 1023) >> 10) << 2;  // blocks per layout thread, <= PM
+  // The layout threads' chunks in registers.  The row holds NKs entries (a
+  // multiple of 4, zero past NK) behind a buffer resource of that size: every
+  // 16-byte piece lies wholly inside or wholly past its end, and the pieces
+  // past it read as 0, so chunk padding is 0 without a per-element test.
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.s + (size_t)lst * NKs), 0, NKs * 4, 0x00020000);
+  int b0[4], nb[4];
+  float sv[4][PM];
 #pragma unroll
-    for (int j = 0; j < C; ++j) { mj[j] = mj_s[j]; coef[j] = coef_s[j]; }
-    constexpr int U = 8;  // blocks per batch: U*C loads in flight
-    float* srow_out = s_out + (size_t)orow * NK;
-#pragma unroll 1
-    for (int b0 = t; b0 < NK; b0 += U * SIP_NT) {
-      float lv[U][C];
+  for (int v = 0; v < 4; ++v) {
+    const int bt = (64 * v + lane) * P;
+    b0[v] = min(NK, bt);
+    nb[v] = min(NK, b0[v] + P) - b0[v];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int e = 0; e < PM; e += 4) {
+      const u32x4 x4 = __builtin_amdgcn_raw_buffer_load_b128(srs, (bt + e) * 4, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const int b = b0 + u * SIP_NT;
-          // (a centroid with coefficient 0 -- an empty cluster, or another
-          // cluster's in a per-cluster sample -- is not read at all)
-          lv[u][j] = (b < NK && coef[j] != 0.f) ? lrow[(size_t)j * NKp + b] : -INFINITY;
-        }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int b = b0 + u * SIP_NT;
-        if (b >= NK) break;
-        const float nk = (float)min(Bk, L - b * Bk);
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const float dl = lv[u][j] - mj[j];
-          if (dl >= -64.f && coef[j] != 0.f) acc = fmaf(coef[j], nk * exp2_split(dl), acc);
-        }
-        s[b] = acc;
-        srow_out[b] = acc;
-      }
+      for (int q = 0; q < 4; ++q) sv[v][e + q] = __uint_as_float(x4[q]);
     }
   }
-  // contiguous chunk of P blocks per thread, P a multiple of 4
-  const int P = ((NK + SIP_NT * 4 - 1) / (SIP_NT * 4)) * 4;
-  const int b0 = min(NK, t * P), b1 = min(NK, b0 + P);
-  __syncthreads();
+  // totals in the layout's thread order
+  auto total4 = [&](const float (&x)[4]) {
+    float t = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t += wave_total(x[v]);
+    return t;
+  };
+  auto total4i = [&](const int (&x)[4]) {
+    int t = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t += wave_total_i(x[v]);
+    return t;
+  };
+  // exclusive prefix of per-thread counts in the layout's thread order, and the total
+  auto scan4 = [&](const int (&x)[4], int (&off)[4]) {
+    int base = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int inc = wave_inclusive_scan(x[v], lane);
+      off[v] = base + inc - x[v];
+      base += __shfl(inc, 63, 64);
+    }
+    return base;
+  };
 
-  // flag: 0 free (pi = s R / S_U), 1 capped (pi = 1), 2 zero (pi = 0), 3 kept, 4 dropped
-  float R = nstar, S_U = 1.f;
-  if (mode == 0) {
-    if (nstar >= (float)NK) {
-      for (int b = b0; b < b1; ++b) flag[b] = 1;
-    } else {
-      const int n = b1 - b0;
-      if (P <= 16) sip_capping<16>(s, b0, n, R, S_U, flag, redf, redi);
-      else if (P <= 24) sip_capping<24>(s, b0, n, R, S_U, flag, redf, redi);
-      else if (P <= 32) sip_capping<32>(s, b0, n, R, S_U, flag, redf, redi);
-      else sip_capping<48>(s, b0, n, R, S_U, flag, redf, redi);
+  uint64_t km[4] = {0ull, 0ull, 0ull, 0ull};  // kept blocks of each chunk
+  if constexpr (MODE == SR_SIP) {
+    float Rb = a.nstar, S_U;
+    float part[4];
+    int cnt[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      part[v] = 0.f;
+      cnt[v] = 0;
+#pragma unroll
+      for (int e = 0; e < PM; ++e) {
+        part[v] += sv[v][e];
+        cnt[v] += sv[v][e] > 0.f;
+      }
     }
-  } else if (mode == 1) {
-    // top-k*: largest bit pattern T with #{s >= T} >= k*, then the lowest-index ties
-    for (int b = b0; b < b1; ++b) flag[b] = 4;
-    if (kstar >= NK) {
-      for (int b = b0; b < b1; ++b) flag[b] = 3;
-    } else if (kstar > 0) {
-      uint32_t lo = 0u, hi = 0x7F800001u;
+    S_U = total4(part);
+    int nfree = total4i(cnt);
 #pragma unroll 1
-      while (hi - lo > 1u) {
-        const uint32_t mid = lo + ((hi - lo) >> 1);
-        int c = 0;
-        for (int b = b0; b < b1; ++b) c += (__float_as_uint(s[b]) >= mid);
-        c = block_sum_i<SIP_NT>(c, redi);
-        if (c >= kstar) lo = mid; else hi = mid;
+    while (nfree > 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        part[v] = 0.f;
+        cnt[v] = 0;
+#pragma unroll
+        for (int e = 0; e < PM; ++e) {
+          const float x = sv[v][e];
+          const bool cp = __fmul_rn(x, Rb) >= S_U;  // never for 0 or -0: S_U > 0 while blocks are free
+          cnt[v] += cp;
+          sv[v][e] = cp ? -0.f : x;
+          part[v] += sv[v][e];
+        }
       }
-      int gt = 0, eq = 0;
-      for (int b = b0; b < b1; ++b) {
-        const uint32_t u = __float_as_uint(s[b]);
-        gt += (u > lo);
-        eq += (u == lo);
-      }
-      const int ngt = block_sum_i<SIP_NT>(gt, redi);
-      int tot;
-      int rank = block_exclusive_scan<SIP_NT>(eq, redi, tot);
-      const int need = kstar - ngt;
-      for (int b = b0; b < b1; ++b) {
-        const uint32_t u = __float_as_uint(s[b]);
-        if (u > lo) flag[b] = 3;
-        else if (u == lo) { if (rank < need) flag[b] = 3; ++rank; }
-      }
+      const float tp = total4(part);
+      const int tc = total4i(cnt);
+      if (tc == 0) break;
+      S_U = tp;
+      Rb -= (float)tc;
+      nfree -= tc;
     }
+    // probabilities (kept in sv) and draws; chunk padding has probability 0
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int g = 0; g < PM; g += 4) {
+        const philox_u4 x = philox4x32_10({(uint32_t)((b0[v] + g) >> 2), ctr1, (uint32_t)bh, a.ctr3}, a.key0, a.key1);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = g + q;
+          const float sc = sv[v][e];
+          const float pr = is_neg_zero(sc) ? 1.f : (sc > 0.f) ? __fdiv_rn(__fmul_rn(sc, Rb), S_U) : 0.f;
+          km[v] |= ((float)(xw[q] >> 8) * 0x1p-24f < pr) ? (1ull << e) : 0ull;
+          sv[v][e] = pr;
+        }
+        // one group at a time: interleaving the unrolled generators would only cost registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
   } else {
-    for (int b = b0; b < b1; ++b) flag[b] = 3;
-  }
-
-  // probabilities, draws, weights
-  int nkept = 0;
-  for (int g = b0; g < b1; g += 4) {
-    philox_u4 x = {0u, 0u, 0u, 0u};
-    const uint32_t ctr1 = per_cluster ? (uint32_t)(i * C + jsel) : (uint32_t)i;
-    if (mode == 0) x = philox4x32_10({(uint32_t)(g >> 2), ctr1, (uint32_t)bh, ctr3}, key0, key1);
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    // the largest bit pattern with #{s >= pattern} >= k* (chunk padding is 0, never counted)
+    uint32_t lo = 0u, hi = 0x7F800001u;
+#pragma unroll 1
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      int c = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int b = g + e;
-      if (b < b1) {
-        float p;
-        if (mode == 0) {
-          const int f = flag[b];
-          p = (f == 1) ? 1.f : (f == 2) ? 0.f : __fdiv_rn(__fmul_rn(s[b], R), S_U);
-          const float u = (float)(xw[e] >> 8) * 0x1p-24f;
-          const bool keep = u < p;
-          flag[b] = keep ? 3 : 4;
-          s[b] = p;  // s is no longer needed: keep pi for the weight
-        } else {
-          p = (flag[b] == 3) ? 1.f : 0.f;
-          s[b] = p;
-        }
-        if (pi_out) pi_out[(size_t)row * NK + b] = p;
-        nkept += (flag[b] == 3);
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < PM; ++e) c += (__float_as_uint(sv[v][e]) >= mid);
+      if (wave_total_i(c) >= a.kstar) lo = mid; else hi = mid;
+    }
+    int gt[4], eq[4], rank[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      gt[v] = 0;
+      eq[v] = 0;
+#pragma unroll
+      for (int e = 0; e < PM; ++e) {
+        const uint32_t u = __float_as_uint(sv[v][e]);
+        gt[v] += (u > lo);
+        eq[v] += (u == lo);
       }
     }
+    // (chunk padding is 0 and comes after every block in thread order: when the
+    // threshold is 0, the ties kept, the lowest-index ones, are all real blocks)
+    const int need = a.kstar - total4i(gt);
+    scan4(eq, rank);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < PM; ++e) {
+        const uint32_t u = __float_as_uint(sv[v][e]);
+        bool keep = u > lo;
+        if (u == lo) keep = rank[v]++ < need;
+        km[v] |= keep ? (1ull << e) : 0ull;
+        sv[v][e] = keep ? 1.f : 0.f;
+      }
   }
-  int total;
-  int off = block_exclusive_scan<SIP_NT>(nkept, redi, total);
-  int32_t* idx_row = kv_idx + (size_t)orow * cap;
-  float* w_row = inv_pi + (size_t)orow * cap;
-  for (int b = b0; b < b1; ++b) {
-    if (flag[b] == 3) {
-      idx_row[off] = b;
-      w_row[off] = (mode == 0) ? __frcp_rn(s[b]) : 1.f;
-      ++off;
+  // list entries in block order
+  int nk4[4], off[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) nk4[v] = __popcll(km[v]);
+  const int total = scan4(nk4, off);
+  int32_t* idx_row = a.kv_idx + (size_t)lst * a.cap;
+  float* w_row = a.inv_pi + (size_t)lst * a.cap;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    int o = off[v];
+#pragma unroll
+    for (int e = 0; e < PM; ++e)
+      if ((km[v] >> e) & 1ull) {
+        idx_row[o] = b0[v] + e;
+        w_row[o] = MODE == SR_SIP ? __frcp_rn(sv[v][e]) : 1.f;
+        ++o;
+      }
+  }
+  if (a.pi_out) {  // inspection (one list per row): stores past NK fall outside the resource
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.pi_out + (size_t)lst * NK), 0, NK * 4, 0x00020000);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < PM; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[v][e]), prs, ((64 * v + lane) * P + e) * 4, 0, 0);
+  }
+  if (lane == 0) a.count[lst] = total;
+}
+
+// Lists that keep every block with probability 1 (SIP with n* >= NK, top-k
+// with k* >= NK, ALL), or none (top-k with k* = 0): one list per workgroup.
+__global__ __launch_bounds__(256) void sel_all_kernel(SelectLaunch a, int keep_all) {
+  const int lst = blockIdx.x;
+  const int C = a.C;
+  const int row = a.per_cluster ? lst / C : lst;
+  const int jc = a.per_cluster ? lst - row * C : 0;
+  const bool empty = !keep_all || (a.per_cluster && a.nj[(size_t)row * C + jc] == 0);
+  const int NK = a.NK;
+  if (!empty) {
+    for (int b = threadIdx.x; b < NK; b += 256) {
+      a.kv_idx[(size_t)lst * a.cap + b] = b;
+      a.inv_pi[(size_t)lst * a.cap + b] = 1.f;
     }
   }
-  if (t == 0) count_out[orow] = total;
+  if (a.pi_out)
+    for (int b = threadIdx.x; b < NK; b += 256) a.pi_out[(size_t)lst * NK + b] = keep_all ? 1.f : 0.f;
+  if (threadIdx.x == 0) a.count[lst] = empty ? 0 : NK;
 }
 
 // ============================================================================= per-cluster union
+constexpr int SIP_NT = 256;
+
 // One workgroup per row: the ascending union of the row's C cluster lists and
 // the weight of every (entry, cluster) pair, 0 where the cluster did not draw
 // the block.  LDS holds one word per KV block: the cluster mask in the low 8
@@ -756,9 +829,31 @@ __global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __
 }
 
 // ============================================================================= launchers
+template <int D>
+static void launch_logit(const SelectLaunch& a, int mode, dim3 grid, hipStream_t st, int M, int NKs, int nsplit,
+                         int per) {
+#define ABSA_LG(MM, CC)                                                                                     \
+  ibcs_logit_kernel<D, MM, CC><<<grid, 256, 0, st>>>(a.kbh, a.mu, a.mz, a.nj, a.s, M, a.NK, NKs, a.NKp, a.L, a.Bq, \
+                                                     a.Bk, nsplit, per, a.alpha)
+  if (mode == LG_MZ) {
+    ABSA_LG(LG_MZ, 1);
+  } else if (mode == LG_SCORE_PC) {
+    ABSA_LG(LG_SCORE_PC, 1);
+  } else {
+    switch (a.C) {
+      case 1: ABSA_LG(LG_SCORE, 1); break;
+      case 2: ABSA_LG(LG_SCORE, 2); break;
+      case 4: ABSA_LG(LG_SCORE, 4); break;
+      default: ABSA_LG(LG_SCORE, 8); break;
+    }
+  }
+#undef ABSA_LG
+}
+
 hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int rows = BH * a.NQ;
+  const int NKs = (a.NK + 3) & ~3;
   // K1
   {
     dim3 grid(a.NKp / 64, BH);
@@ -792,40 +887,42 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // K2b
-  {
-    const int M = a.NQ * a.C;
-    const int mtiles = (M + 127) / 128;
-    int per;
-    const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
-    dim3 grid(mtiles, BH, nsplit);
-    if (a.d == 128)
-      ibcs_logit_kernel<128><<<grid, 256, 0, st>>>(a.kbh, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
-                                                   a.Bk, per, a.alpha);
-    else
-      ibcs_logit_kernel<64><<<grid, 256, 0, st>>>(a.kbh, a.mu, a.logit, a.mz, M, a.NK, a.NKp, a.L,
-                                                  a.Bk, per, a.alpha);
+  // K2b: per-split (max, normaliser) of every centroid, then the scores
+  int per;
+  const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
+  const int M = a.NQ * a.C;
+  const dim3 lgrid((M + 127) / 128, BH, nsplit);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int mode = pass == 0 ? LG_MZ : (a.per_cluster ? LG_SCORE_PC : LG_SCORE);
+    if (a.d == 128) launch_logit<128>(a, mode, lgrid, st, M, NKs, nsplit, per);
+    else launch_logit<64>(a, mode, lgrid, st, M, NKs, nsplit, per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // K3
+  // K3: one list per wave
   {
-    int per;
-    const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
-    const size_t lds = (size_t)a.NK * (sizeof(float) + 1);
-    const dim3 sgrid(rows, a.per_cluster ? a.C : 1);
-#define ABSA_SIP(CC)                                                                                   \
-  sip_kernel<CC><<<sgrid, SIP_NT, lds, st>>>(a.logit, a.mz, nsplit, a.nj, a.s, a.L, a.Bq, a.Bk, a.NK,  \
-                                             a.NKp, a.NQ, a.nstar,                                              \
-                                             a.kstar, a.mode, a.key0, a.key1, a.ctr3, a.count, a.kv_idx, \
-                                             a.inv_pi, a.cap, a.pi_out, a.per_cluster)
-    switch (a.C) {
-      case 1: ABSA_SIP(1); break;
-      case 2: ABSA_SIP(2); break;
-      case 4: ABSA_SIP(4); break;
-      default: ABSA_SIP(8); break;
+    const int nlists = a.per_cluster ? rows * a.C : rows;
+    const bool all = (a.mode == 0 && a.nstar >= (float)a.NK) || a.mode == 2 || (a.mode == 1 && a.kstar >= a.NK);
+    if (all || (a.mode == 1 && a.kstar <= 0)) {
+      sel_all_kernel<<<nlists, 256, 0, st>>>(a, all ? 1 : 0);
+    } else {
+      const dim3 grid((nlists + SR_WAVES - 1) / SR_WAVES);
+      const int P = ((a.NK + 1023) >> 10) << 2;
+      const bool sip = a.mode == 0;
+#define ABSA_SR(PP)                                                                     \
+  if (sip) sip_rows_kernel<PP, SR_SIP><<<grid, 64 * SR_WAVES, 0, st>>>(a, nlists, NKs); \
+  else sip_rows_kernel<PP, SR_TOPK><<<grid, 64 * SR_WAVES, 0, st>>>(a, nlists, NKs)
+      if (P <= 4) { ABSA_SR(4); }
+      else if (P <= 8) { ABSA_SR(8); }
+      else if (P <= 12) { ABSA_SR(12); }
+      else if (P <= 16) { ABSA_SR(16); }
+      else if (P <= 20) { ABSA_SR(20); }
+      else if (P <= 24) { ABSA_SR(24); }
+      else if (P <= 32) { ABSA_SR(32); }
+      else if (P <= 40) { ABSA_SR(40); }
+      else { ABSA_SR(48); }  // NK <= 12288
+#undef ABSA_SR
     }
-#undef ABSA_SIP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -840,14 +937,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
 }
 
 hipError_t configure_select_kernels() {
-  // The SIP kernel keeps one row of scores and flags in LDS: up to 60 KB.
-  hipError_t e;
-#define ABSA_ATTR(CC)                                                                   \
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sip_kernel<CC>),              \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 12288 * 5);      \
-  if (e != hipSuccess) return e;
-  ABSA_ATTR(1) ABSA_ATTR(2) ABSA_ATTR(4) ABSA_ATTR(8)
-#undef ABSA_ATTR
+  // (nothing to configure: the selection kernels use static LDS only)
   return hipSuccess;
 }
 

@@ -133,13 +133,16 @@ absa_status absa_num_blocks(const absa_problem* prob, int32_t* nq, int32_t* nk);
 absa_status absa_select_workspace(const absa_problem* prob, const absa_select_params* params,
                                   size_t* bytes);
 
-/* Byte offsets inside the workspace of absa_select's intermediates, written
- * by every successful absa_select call and left there for inspection:
+/* Byte offsets inside the workspace of absa_select's intermediates, left
+ * there for inspection by a successful absa_select call:
  *   offsets[0]  kbar^T  fp32 [B*H][d][NKp]  block mean keys, NKp = NK rounded up to 64
  *   offsets[1]  mu      fp32 [rows][C][d]   final centroids
  *   offsets[2]  n_j     int32 [rows][C]     final cluster sizes
- *   offsets[3]  s       fp32 [rows][NK]     block scores
- *   offsets[4]  l       fp32 [rows][C][NKp] block logits alpha * mu_j . kbar_b
+ *   offsets[3]  s       fp32 [rows][NKs]    block scores, NKs = NK rounded up to 4 (zeros past NK)
+ *   offsets[4]  SIZE_MAX: the block logits alpha * mu_j . kbar_b are formed on
+ *               chip and never stored
+ * mu, n_j and s are written by every call; kbar^T only by calls with a
+ * non-NULL pi_out (the inspection mode), since the lists do not need it.
  * ([host] pointers; offsets has 5 entries). */
 absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
                                          size_t* offsets);

@@ -107,6 +107,8 @@ def assert_selection_bit_exact(absa, wl: Workload, C: int, Tk: int, mode: int, s
     np.testing.assert_array_equal(mu, res.mu.astype(np.float32))
     nj = wsn[offs[2]: offs[2] + p.rows * C * 4].view(np.int32).reshape(p.rows, C)
     np.testing.assert_array_equal(nj, res.counts)
-    s = wsn[offs[3]: offs[3] + p.rows * NK * 4].view(np.float32).reshape(p.rows, NK)
-    np.testing.assert_array_equal(s, res.scores.astype(np.float32))
+    NKs = -(-NK // 4) * 4    # score rows are padded to a multiple of 4 entries (zeros)
+    s = wsn[offs[3]: offs[3] + p.rows * NKs * 4].view(np.float32).reshape(p.rows, NKs)
+    np.testing.assert_array_equal(s[:, :NK], res.scores.astype(np.float32))
+    assert not s[:, NK:].any()
     return count, kv, w

@@ -114,12 +114,12 @@ def test_workspace_size_and_layout(lib):
     assert lib.absa_select_workspace(ctypes.byref(prob()), ctypes.byref(params()), ctypes.byref(n)) == 0
     offs = (ctypes.c_size_t * 5)()
     assert lib.absa_select_workspace_layout(ctypes.byref(prob()), ctypes.byref(params()), offs) == 0
-    # kbar^T [2][64][64] f32, mu [32][4][64] f32, n_j [32][4] i32, s [32][64] f32,
-    # logits [32][4][64] f32, each 256-aligned
-    assert list(offs) == [0, 32768, 32768 + 32768, 65536 + 512, 65536 + 512 + 8192]
+    # kbar^T [2][64][64] f32, mu [32][4][64] f32, n_j [32][4] i32, s [32][64] f32, each
+    # 256-aligned; no logit region (SIZE_MAX): one-list selection keeps the logits on chip
+    assert list(offs) == [0, 32768, 32768 + 32768, 65536 + 512, 2 ** 64 - 1]
     # + per-split (max, normaliser) of each centroid: 2 splits of the 64 blocks here,
     # + the block means' bf16 heads and tails [2][2][64][64]
-    assert n.value == 65536 + 512 + 8192 + 32 * 4 * 64 * 4 + 32 * 4 * 2 * 8 + 2 * 2 * 64 * 64 * 2
+    assert n.value == 65536 + 512 + 8192 + 32 * 4 * 2 * 8 + 2 * 2 * 64 * 64 * 2
     for bad, code in ((dict(keep=0.0), -1), (dict(keep=1.5), -1), (dict(keep=float("nan")), -1),
                       (dict(clusters=3), -3), (dict(clusters=-1), -1), (dict(kmeans_steps=65), -1),
                       (dict(mode=7), -1), (dict(select_scale_log2=float("inf")), -1)):
@@ -191,8 +191,8 @@ def test_select_noalloc_validation(lib):
     assert call(P, S, FAKE + 8, FAKE, ctypes.byref(lists()), None, None) == _lib.ABSA_ERR_ALIGNMENT
     assert call(P, S, FAKE, FAKE, ctypes.byref(lists(cap=63)), None, None) == _lib.ABSA_ERR_SHAPE
     assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE + 1, None) == _lib.ABSA_ERR_ALIGNMENT
-    # the workspace of the 720p Wan shape with 2 heads (120 MiB) exceeds the fixed 64 MiB buffer
-    p2 = prob(H=2, L=75600, T=21, Hs=45, Ws=80, d=128, q_block=128)
+    # the workspace of the 720p Wan shape with 5 heads (about 87 MiB) exceeds the fixed 64 MiB buffer
+    p2 = prob(H=5, L=75600, T=21, Hs=45, Ws=80, d=128, q_block=128)
     n = ctypes.c_size_t()
     assert lib.absa_select_workspace(ctypes.byref(p2), S, ctypes.byref(n)) == 0 and n.value > 64 << 20
     assert call(ctypes.byref(p2), S, FAKE, FAKE, ctypes.byref(lists(cap=4725)), None, None) == \

@@ -109,7 +109,7 @@ def test_noalloc_binding_and_size_limit(absa):
     torch.cuda.synchronize()
     assert torch.equal(lists.count, ref.count)
     # 720p Wan shape with one head: about 61 MB of selection workspace fits; 4 heads do not
-    big = absa.Problem(1, 4, 75600, 128, 21, 45, 80, 128, 16)
+    big = absa.Problem(1, 5, 75600, 128, 21, 45, 80, 128, 16)
     need = absa.select_workspace_bytes(big, 0.095)
     assert need > 64 << 20
     bl = absa._lib.AbsaBlockList(8, 8, 8, big.nk)   # never dereferenced: rejected before any launch
