@@ -49,8 +49,10 @@ __device__ __forceinline__ philox_u4 philox4x32_10(philox_u4 c, uint32_t k0, uin
   const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
-    const uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+    // (one 32 x 32 -> 64-bit product each: a single v_mad_u64_u32)
+    const uint64_t p0 = (uint64_t)M0 * c.x, p1 = (uint64_t)M1 * c.z;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     philox_u4 n;
     n.x = hi1 ^ c.y ^ k0;
     n.y = lo1;

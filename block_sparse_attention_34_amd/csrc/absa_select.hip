@@ -421,90 +421,126 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
                                          : s_out + ((size_t)bh * M + m0) * NKs;
   const int nrows_w = (MODE == LG_SCORE) ? rows_here / C : rows_here;
 
+  // Score stores go through a buffer resource over the wave's score rows
+  // (nrows_w rows of NKs entries): rows past them fall outside it, and a lane
+  // with nothing to store aims at an offset past its end; such stores are
+  // dropped, so the epilogue below is straight-line code.
+  constexpr uint32_t OOB = 0x7FFFFFF0u;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(SCORE && active ? srow : s_out), 0, SCORE && active ? nrows_w * NKs * 4 : 0, 0x00020000);
+  // The logits of one tile (its B operands from LDS buffer buf)
+  auto logits = [&](int buf) {
+    const unsigned char* kl = &kt[buf][lane * 16];
+    bf16x8 bhi[KS], blo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bhi[ks] = *reinterpret_cast<const bf16x8*>(kl + ks * 2048);
+      blo[ks] = *reinterpret_cast<const bf16x8*>(kl + ks * 2048 + 1024);
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], bhi[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], blo[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], bhi[ks], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  // What a tile's logits leave (tile0 - 1 stands for "no tile yet": every block is padding)
+  auto epilogue = [&](const f32x16& acc, int tile) {
+    const int b = tile * 32 + n;
+    const bool started = tile >= tile0;
+    const bool bv = started && b < NK;
+    const float nk = (float)min(Bk, L - b * Bk);
+    if constexpr (SCORE) {
+      // lane (h, n) register r: centroid m0 + 8 (r/4) + 4 h + r%4 against block b
+      const bool bs = started && b < NKs;  // the row's entry b exists (zero past NK)
+      float term[16];
+      uint32_t ok = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dl = fmaf(alpha, acc[r], -mj[r]);
+        const bool on = dl >= -64.f && cf[r] != 0.f;
+        term[r] = on ? nk * exp2_split(dl) : 0.f;
+        ok |= on ? (1u << r) : 0u;
+      }
+      auto put_score = [&](int rl, float sv, bool lane_stores) {
+        const uint32_t off = (bs && lane_stores) ? (uint32_t)(rl * NKs + b) * 4u : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bv ? sv : 0.f), srs, off, 0, 0);
+      };
+      if constexpr (MODE == LG_SCORE_PC) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          put_score(8 * (r >> 2) + 4 * h + (r & 3), ((ok >> r) & 1u) ? fmaf(cf[r], term[r], 0.f) : 0.f, true);
+      } else if constexpr (C <= 4) {
+        // the C centroids of a row are consecutive registers of one lane
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int gg = 0; gg < 4 / C; ++gg) {
+            float sv = 0.f;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+              const int r = 4 * q + gg * C + j;
+              sv = ((ok >> r) & 1u) ? fmaf(cf[r], term[r], sv) : sv;
+            }
+            put_score((8 * q + 4 * h + gg * C) / C, sv, true);
+          }
+      } else {
+        // C = 8: row q's centroids 0..3 sit in half-wave 0 (registers 4 q ..),
+        // 4..7 in half-wave 1; half 1 continues the sum half 0 started
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float sv = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sv = (h == 0 && ((ok >> (4 * q + j)) & 1u)) ? fmaf(cf[4 * q + j], term[4 * q + j], sv) : sv;
+          sv = __shfl_xor(sv, 32, 64);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sv = ((ok >> (4 * q + j)) & 1u) ? fmaf(cf[4 * q + j], term[4 * q + j], sv) : sv;
+          put_score(q, sv, h == 1);
+        }
+      }
+    } else {
+      // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
+      // and 2^(l - max) differs from 1, so one exp2 per logit suffices: a new
+      // max gives Z e + nk, an old one Z + nk e.  Padding blocks (b >= NK)
+      // enter as l = -inf, which changes neither m nor Z; fma(alpha, acc, 0)
+      // rounds like the product alone.
+      const float pad = bv ? 0.f : -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float l = fmaf(alpha, acc[r], pad);
+        const float dd = fabsf(rm[r] - l);
+        const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
+        const bool up = l > rm[r];
+        rz[r] = up ? fmaf(rz[r], e, nk) : fmaf(nk, e, rz[r]);
+        rm[r] = fmaxf(rm[r], l);
+      }
+    }
+  };
+  // Software pipeline by one tile: the matrix core works on tile t while the
+  // vector units finish tile t - 1, in the same stretch of straight-line code.
+  f32x16 accp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accp[r] = 0.f;
   auto body = [&](int tile, const u32x4 (&sput)[NST], u32x4 (&sfetch)[NST]) {
     const int buf = (tile - tile0) & 1;
     __syncthreads();
     if (tile + 2 < tile1) fetch(sfetch, tile + 2);
     if (active) {
-      const unsigned char* kl = &kt[buf][lane * 16];
-      f32x16 acc;
+      const f32x16 accn = logits(buf);
+      epilogue(accp, tile - 1);
+      accp = accn;
+      // interleave: the tile's operand reads first, then each product with a share of the epilogue
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 bhi = *reinterpret_cast<const bf16x8*>(kl + ks * 2048);
-        const bf16x8 blo = *reinterpret_cast<const bf16x8*>(kl + ks * 2048 + 1024);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], bhi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], blo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], bhi, acc, 0, 0, 0);
-      }
-      const int b = tile * 32 + n;
-      const bool bv = b < NK;
-      const float nk = (float)min(Bk, L - b * Bk);
-      if constexpr (SCORE) {
-        // lane (h, n) register r: centroid m0 + 8 (r/4) + 4 h + r%4 against block b
-        float term[16];
-        uint32_t ok = 0u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float dl = alpha * acc[r] - mj[r];
-          const bool on = dl >= -64.f && cf[r] != 0.f;
-          term[r] = on ? nk * exp2_split(dl) : 0.f;
-          ok |= on ? (1u << r) : 0u;
-        }
-        if constexpr (MODE == LG_SCORE_PC) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = 8 * (r >> 2) + 4 * h + (r & 3);
-            const float sv = ((ok >> r) & 1u) ? fmaf(cf[r], term[r], 0.f) : 0.f;
-            if (b < NKs && rl < nrows_w) srow[(size_t)rl * NKs + b] = bv ? sv : 0.f;
-          }
-        } else if constexpr (C <= 4) {
-          // the C centroids of a row are consecutive registers of one lane
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int gg = 0; gg < 4 / C; ++gg) {
-              float sv = 0.f;
-#pragma unroll
-              for (int j = 0; j < C; ++j) {
-                const int r = 4 * q + gg * C + j;
-                if ((ok >> r) & 1u) sv = fmaf(cf[r], term[r], sv);
-              }
-              const int rl = (8 * q + 4 * h + gg * C) / C;
-              if (b < NKs && rl < nrows_w) srow[(size_t)rl * NKs + b] = bv ? sv : 0.f;
-            }
-        } else {
-          // C = 8: row q's centroids 0..3 sit in half-wave 0 (registers 4 q ..),
-          // 4..7 in half-wave 1; half 1 continues the sum half 0 started
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float sv = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (h == 0 && ((ok >> (4 * q + j)) & 1u)) sv = fmaf(cf[4 * q + j], term[4 * q + j], sv);
-            sv = __shfl_xor(sv, 32, 64);
-            if (h == 1) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if ((ok >> (4 * q + j)) & 1u) sv = fmaf(cf[4 * q + j], term[4 * q + j], sv);
-              if (b < NKs && q < nrows_w) srow[(size_t)q * NKs + b] = bv ? sv : 0.f;
-            }
-          }
-        }
-      } else {
-        // Online (m, Z): with d = |m - l| only one of the two factors 2^(m - max)
-        // and 2^(l - max) differs from 1, so one exp2 per logit suffices.  Padding
-        // blocks (b >= NK) enter as l = -inf, which changes neither m nor Z.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float l = bv ? alpha * acc[r] : -INFINITY;
-          const float dd = fabsf(rm[r] - l);
-          const float e = dd <= 64.f ? exp2_split(-dd) : 0.f;
-          const bool up = l > rm[r];
-          rz[r] = fmaf(rz[r], up ? e : 1.f, up ? nk : nk * e);
-          rm[r] = up ? l : rm[r];
-        }
+      for (int i = 0; i < 3 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
     }
     if (tile + 1 < tile1) put(sput, buf ^ 1);
@@ -514,6 +550,7 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
     body(tile, stA, stB);
     if (tile + 1 < tile1) body(tile + 1, stB, stA);
   }
+  if (active) epilogue(accp, tile1 - 1);
   if constexpr (!SCORE) {
     if (!active) return;
     // combine over the 32 blocks (lanes) of each half-wave and write this split's
