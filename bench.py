@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=1920)
     ap.add_argument("--cpu-single-rows", type=int, default=240, help="rows of the one-thread oracle sample")
+    ap.add_argument("--kernels-once", action="store_true",
+                    help="for counter collection: one selection, two sparse attentions and one dense attention, "
+                         "then exit (no JSON line)")
     ap.add_argument("--extra", action="store_true", help="also time the dense kernel, the FP8 variant and per-cluster lists")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the JSON line: accuracy and time of SIP / top-k / block-size / prior-art "
@@ -203,6 +206,15 @@ def ablation(args):
             for kp, e in sip.items()) + "\n", flush=True)
 
 
+def _logit_splits(NQ, C, BH, NKp):
+    """Block-range splits of the logit product (the library's rule: at least ~2048 workgroups)."""
+    mtiles = (NQ * C + 127) // 128
+    ntile = NKp // 32
+    nsplit = min(max((2048 + mtiles * BH - 1) // (mtiles * BH), 1), ntile)
+    per = (ntile + nsplit - 1) // nsplit
+    return (ntile + per - 1) // per
+
+
 def attend_source_digest():
     """First 16 hex digits of the sha256 over the gather-attention kernel sources."""
     import hashlib
@@ -318,6 +330,14 @@ def main():
         absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
         absa.attend(p, q, k, v, lists, out=o)
 
+    if args.kernels_once:
+        step()
+        absa.attend(p, q, k, v, lists, out=o)
+        absa.dense(p, q, k, v, out=o)
+        torch.cuda.synchronize()
+        print("[bench] kernels-once done", file=sys.stderr, flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -388,6 +408,28 @@ def main():
         "kept_fraction": float(count.double().mean()) / NK,
         "gather_GBs": alg_bytes / (att_avg * 1e-3) / 1e9,
     }
+    # the selection kernel by kernel (HIP events between its launches), with the bytes each must
+    # move at least: its inputs read once and its outputs written once
+    prof = [absa.select_profile(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)[1] for _ in range(3)]
+    C, BH, rows_n = 4, p.B * p.H, p.rows
+    NKp, NKs = -(-NK // 64) * 64, -(-NK // 4) * 4
+    nsplit = _logit_splits(NQ, C, BH, NKp)
+    qk_bytes = BH * L * d * 2
+    kbh_bytes = BH * NKp * d * 4
+    mu_bytes = rows_n * C * (d + 1) * 4
+    mz_bytes = rows_n * C * nsplit * 8
+    s_bytes = rows_n * NKs * 4
+    list_bytes = float(count.sum()) * 8 + rows_n * 4
+    alg = {"block means": qk_bytes + kbh_bytes, "k-means": qk_bytes + mu_bytes,
+           "logit normalisers": kbh_bytes + mu_bytes + mz_bytes,
+           "scores": kbh_bytes + mu_bytes + mz_bytes + s_bytes, "sampling": s_bytes + list_bytes}
+    sk = {}
+    for name in absa.SELECT_KERNELS:
+        t = sum(pr[name] for pr in prof) / len(prof)
+        sk[name] = {"ms": t, "bytes": alg[name], "GBs": alg[name] / (t * 1e-3) / 1e9,
+                    "hbm_frac": alg[name] / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    line["select_kernels"] = sk
+    line["select_alg_bytes"] = 2 * qk_bytes + list_bytes
     # accuracy of the timed step's output against dense attention, and of top-k lists of the same
     # budget (after the timed region)
     o_dense = torch.empty_like(o)

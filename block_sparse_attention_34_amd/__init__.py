@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
 
 __all__ = [
-    "Problem", "BlockLists", "select", "select_noalloc", "attend", "dense", "num_blocks", "select_workspace_bytes",
+    "Problem", "BlockLists", "select", "select_noalloc", "select_profile", "SELECT_KERNELS", "attend", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
     "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
     "ClusterLists", "alloc_cluster_lists", "select_clusters_workspace_bytes", "select_clusters", "attend_clusters",
@@ -208,6 +208,32 @@ def select_noalloc(prob: Problem, q, k, keep: float, lists: BlockLists, *, clust
                                        ctypes.byref(bl), pi.data_ptr() if pi is not None else None, _stream())
     _lib.check(st, "absa_select_noalloc")
     return lists, pi
+
+
+SELECT_KERNELS = ("block means", "k-means", "logit normalisers", "scores", "sampling")
+
+
+def select_profile(prob: Problem, q, k, keep: float, *, clusters: int = 0, kmeans_steps: int = 0,
+                   select_scale_log2: float = 0.0, seed: int = 0, stream_id: int = 0, mode="sip",
+                   lists: Optional[BlockLists] = None, workspace=None):
+    """One ``select`` timed kernel by kernel (HIP events on the current stream; waits for it).
+    Returns (lists, {kernel name: ms}) with the names of SELECT_KERNELS."""
+    import torch
+    _check_qkv(prob, q, k)
+    lists = alloc_lists(prob, q.device) if lists is None else lists
+    _check_lists(prob, lists, q.device, need_cap_nk=True)
+    nbytes = select_workspace_bytes(prob, keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    sp = _params(keep, clusters, kmeans_steps, select_scale_log2, seed, stream_id, mode)
+    bl = lists.c()
+    ms = (ctypes.c_float * len(SELECT_KERNELS))()
+    st = library().absa_select_profile(ctypes.byref(p), ctypes.byref(sp), q.data_ptr(), k.data_ptr(),
+                                       ctypes.byref(bl), workspace.data_ptr(), workspace.numel(), _stream(), ms,
+                                       len(SELECT_KERNELS))
+    _lib.check(st, "absa_select_profile")
+    return lists, dict(zip(SELECT_KERNELS, (float(x) for x in ms)))
 
 
 def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):

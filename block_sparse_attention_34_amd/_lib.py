@@ -21,7 +21,7 @@ EXPORTED = (
     "absa_select_workspace_layout", "absa_select", "absa_attend", "absa_dense",
     "absa_fp8_workspace", "absa_quantize_fp8", "absa_attend_fp8",
     "absa_select_clusters_workspace", "absa_select_clusters", "absa_attend_clusters",
-    "absa_select_noalloc",
+    "absa_select_noalloc", "absa_select_profile",
 )
 
 
@@ -98,6 +98,9 @@ def load() -> ctypes.CDLL:
     lib.absa_select.argtypes = [P, SP, vp, vp, BL, vp, vp, sz, vp]
     lib.absa_select_noalloc.restype = ctypes.c_int
     lib.absa_select_noalloc.argtypes = [P, SP, vp, vp, BL, vp, vp]
+    lib.absa_select_profile.restype = ctypes.c_int
+    lib.absa_select_profile.argtypes = [P, SP, vp, vp, BL, vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.c_int32]
     lib.absa_attend.restype = ctypes.c_int
     lib.absa_attend.argtypes = [P, vp, vp, vp, BL, vp, vp]
     lib.absa_dense.restype = ctypes.c_int

@@ -368,6 +368,39 @@ absa_status absa_select_noalloc(const absa_problem* prob, const absa_select_para
   return run_select(prob, params, dm, sp, w, q, k, out, pi_out, ws, stream);
 }
 
+absa_status absa_select_profile(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                const void* k, const absa_blocklist* out, void* workspace, size_t workspace_bytes,
+                                void* stream, float* kernel_ms, int32_t n_ms) {
+  if (!kernel_ms || n_ms < 0) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  SelParams sp;
+  WsLayout w;
+  absa_status st = check_select(prob, params, q, k, out, nullptr, &dm, &sp, &w);
+  if (st != ABSA_OK) return st;
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, kWsAlign)) return ABSA_ERR_ALIGNMENT;
+  std::call_once(g_attr_once, [] { g_attr_err = absa::configure_select_kernels(); });
+  if (g_attr_err != hipSuccess) return ABSA_ERR_HIP;
+  hipEvent_t ev[absa::kSelectEvents];
+  int made = 0;
+  hipError_t e = hipSuccess;
+  for (; made < absa::kSelectEvents && e == hipSuccess; ++made) e = hipEventCreate(&ev[made]);
+  if (e == hipSuccess) {
+    absa::SelectLaunch a = select_launch(prob, params, dm, sp, w, static_cast<char*>(workspace), q, k);
+    a.count = out->count;
+    a.kv_idx = out->kv_idx;
+    a.inv_pi = out->inv_pi;
+    a.cap = out->cap;
+    a.kbarT = nullptr;
+    e = absa::launch_select(a, static_cast<hipStream_t>(stream), ev);
+  }
+  if (e == hipSuccess) e = hipEventSynchronize(ev[absa::kSelectEvents - 1]);
+  for (int i = 0; e == hipSuccess && i + 1 < absa::kSelectEvents && i < n_ms; ++i)
+    e = hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]);
+  for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
 absa_status absa_select_clusters_workspace(const absa_problem* prob, const absa_select_params* params,
                                            size_t* bytes) {
   if (!bytes) return ABSA_ERR_INVALID_ARG;

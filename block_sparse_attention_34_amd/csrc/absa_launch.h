@@ -95,7 +95,10 @@ inline int logit_splits(int NQ, int C, int BH, int NKp, int* tiles_per_split) {
   return (ntile_all + per - 1) / per;
 }
 
-hipError_t launch_select(const SelectLaunch& a, hipStream_t st);
+// ev: null, or kSelectEvents events recorded on st before the first kernel and
+// after each of the selection's kernels (measurement only)
+constexpr int kSelectEvents = 6;
+hipError_t launch_select(const SelectLaunch& a, hipStream_t st, hipEvent_t* ev = nullptr);
 hipError_t configure_select_kernels();
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense);
 hipError_t launch_attend_pp(const AttendLaunch& a, hipStream_t st, bool dense);

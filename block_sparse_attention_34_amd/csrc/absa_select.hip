@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256) void ibcs_kmeans_mfma_kernel(const uint16_t* _
 //  * LG_SCORE_PC: per-cluster lists: each cluster's own score
 //      s_jb = nk_b 2^(l_jb - m_j) / Z_j  into s[row C + j][NKs].
 // Score rows have NKs = NK rounded up to 4 entries, the tail set to 0.
-// Grid (ceil(M/128), BH, nsplit): split z covers a contiguous range of 32-block
-// tiles.
+// Grid: ceil(M/128) x BH x nsplit workgroups in one dimension; split z covers a
+// contiguous range of 32-block tiles.
 constexpr int LG_MZ = 0, LG_SCORE = 1, LG_SCORE_PC = 2;
 
 template <int D, int MODE, int C>
@@ -336,10 +336,17 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (scalar) index
   const int h = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.y;
-  const int m0 = blockIdx.x * 128 + w * 32;
+  // Workgroups are dealt to the 8 XCDs in turn; each XCD takes a contiguous
+  // range of (centroid tile, head, split) triples, centroid tile fastest, so the
+  // workgroups that read one head's split of the block means share an L2.
+  const int ntm = (M + 127) / 128;
+  const int G = (int)gridDim.x, g = (int)blockIdx.x, xcd = g & 7;
+  const int nbh = G / (ntm * nsplit);
+  const int u = xcd * (G >> 3) + min(xcd, G & 7) + (g >> 3);
+  const int mt = u % ntm, bh = (u / ntm) % nbh, zs = u / (ntm * nbh);
+  const int m0 = mt * 128 + w * 32;
   const int NT = NKp / 32;
-  const int tile0 = blockIdx.z * tiles_per_split;
+  const int tile0 = zs * tiles_per_split;
   const int tile1 = min(NT, tile0 + tiles_per_split);
   const bool active = m0 < M;  // waves without centroids still stage tiles
   const unsigned char* kb = reinterpret_cast<const unsigned char*>(kbh) + (size_t)bh * NT * TB;
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
     // max, normaliser and score coefficient of the workgroup's 128 centroids:
     // (n_j/n)/Z_j for the mixture, 1/Z_j for a cluster's own score
     if (t < 128) {
-      const int m = blockIdx.x * 128 + t;
+      const int m = mt * 128 + t;
       float mx = -INFINITY, coef = 0.f;
       if (m < M) {
         const float2* pz = mz + ((size_t)bh * M + m) * nsplit;
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
         rm[r] = mn;
       }
       const int m = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (n == 0 && m < M) mz[((size_t)bh * M + m) * nsplit + blockIdx.z] = make_float2(rm[r], rz[r]);
+      if (n == 0 && m < M) mz[((size_t)bh * M + m) * nsplit + zs] = make_float2(rm[r], rz[r]);
     }
   }
 }
@@ -887,10 +894,16 @@ static void launch_logit(const SelectLaunch& a, int mode, dim3 grid, hipStream_t
 #undef ABSA_LG
 }
 
-hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
+hipError_t launch_select(const SelectLaunch& a, hipStream_t st, hipEvent_t* ev) {
+  int nev = 0;
+  auto mark = [&]() -> hipError_t { return ev ? hipEventRecord(ev[nev++], st) : hipSuccess; };
   const int BH = a.B * a.H;
   const int rows = BH * a.NQ;
   const int NKs = (a.NK + 3) & ~3;
+  {
+    hipError_t e = mark();
+    if (e != hipSuccess) return e;
+  }
   // K1
   {
     dim3 grid(a.NKp / 64, BH);
@@ -899,6 +912,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     else
       kv_block_mean_kernel<64><<<grid, 256, 0, st>>>(a.k, a.kbarT, a.kbh, a.L, a.Bk, a.NK, a.NKp);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark();
     if (e != hipSuccess) return e;
   }
   // K2a
@@ -922,18 +936,20 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     }
 #undef ABSA_KM
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark();
     if (e != hipSuccess) return e;
   }
   // K2b: per-split (max, normaliser) of every centroid, then the scores
   int per;
   const int nsplit = logit_splits(a.NQ, a.C, BH, a.NKp, &per);
   const int M = a.NQ * a.C;
-  const dim3 lgrid((M + 127) / 128, BH, nsplit);
+  const dim3 lgrid(((M + 127) / 128) * BH * nsplit);
   for (int pass = 0; pass < 2; ++pass) {
     const int mode = pass == 0 ? LG_MZ : (a.per_cluster ? LG_SCORE_PC : LG_SCORE);
     if (a.d == 128) launch_logit<128>(a, mode, lgrid, st, M, NKs, nsplit, per);
     else launch_logit<64>(a, mode, lgrid, st, M, NKs, nsplit, per);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark();
     if (e != hipSuccess) return e;
   }
   // K3: one list per wave
@@ -961,6 +977,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
 #undef ABSA_SR
     }
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && !a.per_cluster) e = mark();
     if (e != hipSuccess) return e;
   }
   // union of the per-cluster lists
@@ -968,6 +985,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st) {
     cluster_union_kernel<<<rows, SIP_NT, (size_t)a.NK * sizeof(uint32_t), st>>>(
         a.count, a.kv_idx, a.inv_pi, a.cap, a.C, a.NK, a.ucount, a.uidx, a.uw, a.ucap);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

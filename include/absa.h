@@ -173,6 +173,17 @@ absa_status absa_select(const absa_problem* prob, const absa_select_params* para
 absa_status absa_select_noalloc(const absa_problem* prob, const absa_select_params* params, const void* q,
                                 const void* k, const absa_blocklist* out, float* pi_out, void* stream);
 
+/* Measurement: absa_select (without probabilities) with a HIP event recorded
+ * on `stream` before and after each of its five kernels -- block means, k-means,
+ * logit normalisers, scores, sampling -- and the time of each, in ms and in that
+ * order, written to the first min(n_ms, 5) entries of kernel_ms ([host]).  The
+ * call waits for the selection to finish; the lists are those absa_select
+ * gives.  Arguments and errors as absa_select; n_ms < 0 or a NULL kernel_ms
+ * is ABSA_ERR_INVALID_ARG, a failed event call ABSA_ERR_HIP. */
+absa_status absa_select_profile(const absa_problem* prob, const absa_select_params* params, const void* q,
+                                const void* k, const absa_blocklist* out, void* workspace, size_t workspace_bytes,
+                                void* stream, float* kernel_ms, int32_t n_ms);
+
 /* Block-sparse attention over given lists (the estimate above): for every
  * valid query of row r, attends to the keys of the blocks listed for r with
  * their weights.  o is [B, H, L, d] (fp32, or bf16 if out_bf16), 16-byte

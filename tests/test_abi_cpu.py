@@ -202,6 +202,21 @@ def test_select_noalloc_validation(lib):
         assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), None, None) == _lib.ABSA_ERR_HIP
 
 
+def test_select_profile_validation(lib):
+    n = ctypes.c_size_t()
+    lib.absa_select_workspace(ctypes.byref(prob()), ctypes.byref(params()), ctypes.byref(n))
+    ws = n.value
+    P, S = ctypes.byref(prob()), ctypes.byref(params())
+    ms = (ctypes.c_float * 5)()
+    call = lib.absa_select_profile
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE, ws, None, None, 5) == _lib.ABSA_ERR_INVALID_ARG
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE, ws, None, ms, -1) == _lib.ABSA_ERR_INVALID_ARG
+    assert call(P, S, None, FAKE, ctypes.byref(lists()), FAKE, ws, None, ms, 5) == _lib.ABSA_ERR_INVALID_ARG
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists(cap=63)), FAKE, ws, None, ms, 5) == _lib.ABSA_ERR_SHAPE
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE, ws - 1, None, ms, 5) == _lib.ABSA_ERR_WORKSPACE
+    assert call(P, S, FAKE, FAKE, ctypes.byref(lists()), FAKE + 16, ws, None, ms, 5) == _lib.ABSA_ERR_ALIGNMENT
+
+
 def fp8_ops(**kw):
     base = dict(q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, kbar=FAKE, v8t=FAKE, sv=FAKE, mu=FAKE)
     base.update(kw)
