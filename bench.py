@@ -55,10 +55,11 @@ def ablation(args):
     """Error of the estimator against dense attention (rel-L2 over the whole output) and the time of
     selection and attention, for: SIP at three budgets and three seeds, top-k truncation at the same
     budgets, the KV block size at a 10% budget, and the coarse prior-art arm (one mean query per block,
-    top-k, 64-key blocks).  On three inputs: the workload as generated (its 10x-norm outlier tokens act
-    as attention sinks: about one effective key per query), and the same recipe without outlier tokens
-    with queries scaled by 1/4 and by 1/8 (more diffuse attention); the effective number of keys per
-    query (exp of the softmax entropy, mean over sampled rows) is printed for each.
+    top-k, 64- and 128-key blocks, the latter a whole 128 x 128 tile).  On three inputs: the workload
+    as generated (its 10x-norm outlier tokens act as attention sinks: about one effective key per
+    query), and the same recipe without outlier tokens with queries scaled by 1/4 and by 1/8 (more
+    diffuse attention); the effective number of keys per query (exp of the softmax entropy, mean
+    over sampled rows) is printed for each.
     Times are HIP-event means over 5 launches after 2 warm-ups."""
     import numpy as np
     import torch
@@ -127,11 +128,12 @@ def ablation(args):
             for seed in (0, 1, 2):
                 run("IBCS+SIP", 16, keep, "sip", seed)
             run("IBCS+top-k", 16, keep, "topk", 0)
-        for Bk in (16, 32, 64):
+        for Bk in (16, 32, 64, 128):
             run("IBCS+SIP", Bk, 0.10, "sip", 0)
             run("IBCS+top-k", Bk, 0.10, "topk", 0)
-        run("mean query+top-k (prior art)", 64, 0.10, "topk", 0, clusters=1)
-        run("mean query+SIP", 64, 0.10, "sip", 0, clusters=1)
+        for Bk in (64, 128):
+            run("mean query+top-k (prior art)", Bk, 0.10, "topk", 0, clusters=1)
+            run("mean query+SIP", Bk, 0.10, "sip", 0, clusters=1)
         # the IBCS knobs at Bk 16, keep 9.5%: cluster count (C = 4 is above) and k-means steps
         for C in (1, 2, 8):
             run("IBCS+SIP, C sweep", 16, 0.095, "sip", 0, clusters=C)

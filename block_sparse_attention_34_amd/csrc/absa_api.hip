@@ -18,7 +18,7 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
-constexpr int kMaxNK = 12288;  // selection keeps one row of scores in LDS
+constexpr int kMaxNK = 12288;  // the sampler holds a row in the registers of at most 4 waves, the union a word per block in LDS
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -40,7 +40,8 @@ absa_status check_problem(const absa_problem* p, Dims* dm) {
   if (p->out_bf16 != 0 && p->out_bf16 != 1) return ABSA_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return ABSA_ERR_UNSUPPORTED;
   if (p->q_block != 64 && p->q_block != 128) return ABSA_ERR_UNSUPPORTED;
-  if (p->kv_block != 16 && p->kv_block != 32 && p->kv_block != 64) return ABSA_ERR_UNSUPPORTED;
+  if (p->kv_block != 16 && p->kv_block != 32 && p->kv_block != 64 && p->kv_block != 128)
+    return ABSA_ERR_UNSUPPORTED;
   const int64_t BH = (int64_t)p->B * p->H;
   // element offsets are computed in 64-bit; row and key indices in 32-bit
   if (BH * (int64_t)p->L * p->d > (int64_t(1) << 46)) return ABSA_ERR_UNSUPPORTED;

@@ -6,7 +6,7 @@
 //
 // One workgroup owns one row (b, h, query block): BQ/32 waves, each holding 32
 // queries.  The row's KV blocks are gathered 64 keys at a time (64/BK list
-// entries per tile) from HBM straight into LDS.  Per tile and wave:
+// entries per tile; a 128-key block is two tiles) from HBM straight into LDS.  Per tile and wave:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = the
 //                 wave's queries, kept in registers for the whole row);
 //   t = S * scale*log2(e) + log2(w_b)   (w_b the block's weight; -inf for
@@ -48,12 +48,18 @@ __global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a)
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
   constexpr int KPI = 64 / CPR;        // key rows covered by one wave-wide 16-byte load
   constexpr int NCH = 64 * CPR / NT;   // wave-wide loads per thread per tile and tensor
-  constexpr int SPT = 64 / BK;         // list entries per 64-key tile
+  constexpr int SPT = BK >= 64 ? 1 : 64 / BK;  // list entries per 64-key tile
+  constexpr int TPE = BK > 64 ? BK / 64 : 1;   // 64-key tiles per list entry (128-key blocks: 2)
   constexpr int KS = D / 16;           // k-steps of the QK product
   constexpr int DB = D / 32;           // 32-wide d blocks of O
   constexpr int TILE = 64 * D * 2;
   constexpr float TAU = 8.f;           // the running max moves only when exceeded by this
   static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
+  static_assert(BK <= 64 || BK % 64 == 0, "a block larger than a tile spans whole tiles");
+  static_assert(!(DENSE && BK != 64), "the dense path walks 64-key tiles");
+  // list entry of key k (0..63) of a tile, and that key's row inside its block
+  auto entry_of = [](int tile, int k) { return TPE > 1 ? tile / TPE : tile * SPT + k / BK; };
+  auto row_in_block = [](int tile, int k) { return TPE > 1 ? (tile % TPE) * 64 + k : k % BK; };
 
   __shared__ __attribute__((aligned(16))) unsigned char k_s0[TILE];
   __shared__ __attribute__((aligned(16))) unsigned char k_s1[TILE];
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a)
   } else {
     nblk = a.count[row];
     nblk = nblk < 0 ? 0 : (nblk > a.cap ? a.cap : nblk);
-    T = (nblk + SPT - 1) / SPT;
+    T = TPE > 1 ? nblk * TPE : (nblk + SPT - 1) / SPT;
     lidx = a.kv_idx + (size_t)row * a.cap;
     lw = a.inv_pi + (size_t)row * a.cap;
   }
@@ -157,10 +163,10 @@ __global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a)
     if constexpr (!DENSE) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int e = tile * SPT + ((j * NW + wid) * KPI) / BK;
+        const int e = entry_of(tile, (j * NW + wid) * KPI);
         E.blk[j] = lidx[e < nblk ? e : nblk - 1];
       }
-      const int e = tile * SPT + lane / BK;
+      const int e = entry_of(tile, lane);
       const int ec = e < nblk ? e : nblk - 1;
       E.bblk = lidx[ec];
       E.bw = lw[ec];
@@ -170,13 +176,14 @@ __global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a)
   auto bases = [&](const Entries& E, int tile, uint32_t (&base)[NCH]) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int e = tile * SPT + ((j * NW + wid) * KPI) / BK;
+      const int e = entry_of(tile, (j * NW + wid) * KPI);
       if constexpr (DENSE) {
         base[j] = (uint32_t)e * (BK * D * 2);
       } else {
         const int blk = __builtin_amdgcn_readfirstlane(E.blk[j]);
         const bool ok = e < nblk && blk >= 0 && blk < a.NK;
-        base[j] = ok ? (uint32_t)blk * (BK * D * 2) : OOB;
+        // (a block of several tiles: this tile's keys start (tile % TPE) * 64 rows into it)
+        base[j] = ok ? (uint32_t)blk * (BK * D * 2) + (uint32_t)(row_in_block(tile, 0) * D * 2) : OOB;
       }
     }
   };
@@ -192,10 +199,10 @@ __global__ __launch_bounds__(BQ * 2, BQ / 64) void attend_kernel(AttendLaunch a)
   };
   auto put_bias = [&](int slot, const Entries& E, int tile) {
     if (tid < 64) {
-      const int e = tile * SPT + tid / BK;
+      const int e = entry_of(tile, tid);
       const int blk = DENSE ? e : E.bblk;
       const bool ok = DENSE ? true : (e < nblk && blk >= 0 && blk < a.NK);
-      const int key = blk * BK + tid % BK;
+      const int key = blk * BK + row_in_block(tile, tid);
       bias_s[slot][tid] = (ok && key < a.L) ? (DENSE ? 0.f : __log2f(E.bw)) : -INFINITY;
       const unsigned long long any_tail = __ballot(ok && key >= a.L);
       if (lane == 0) tail_s[slot] = any_tail != 0ull;
@@ -447,7 +454,8 @@ static hipError_t launch_bk(const AttendLaunch& a, hipStream_t st, bool dense) {
   switch (a.Bk) {
     case 16: return launch_t<D, BQ, 16, false>(a, st);
     case 32: return launch_t<D, BQ, 32, false>(a, st);
-    default: return launch_t<D, BQ, 64, false>(a, st);
+    case 64: return launch_t<D, BQ, 64, false>(a, st);
+    default: return launch_t<D, BQ, 128, false>(a, st);
   }
 }
 

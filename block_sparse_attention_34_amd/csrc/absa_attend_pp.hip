@@ -41,12 +41,15 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   constexpr int CPR = D / 8;           // 16-byte chunks per key row
   constexpr int KPI = 64 / CPR;        // key rows covered by one wave-wide 16-byte load
   constexpr int NCH = 64 * CPR / HT;   // wave-wide loads per thread per tile and tensor
-  constexpr int SPT = 64 / BK;         // list entries per 64-key tile
+  constexpr int SPT = BK >= 64 ? 1 : 64 / BK;  // list entries per 64-key tile
+  constexpr int TPE = BK > 64 ? BK / 64 : 1;   // 64-key tiles per list entry (128-key blocks: 2)
   constexpr int KS = D / 16;           // k-steps of the QK product
   constexpr int DB = D / 32;           // 32-wide d blocks of O
   constexpr int TILE = 64 * D * 2;
   constexpr float TAU = 8.f;           // the running max moves only when exceeded by this
   static_assert(BK % KPI == 0, "a wave-wide load must stay inside one block");
+  static_assert(BK <= 64 || BK % 64 == 0, "a block larger than a tile spans whole tiles");
+  static_assert(!(DENSE && BK != 64), "the dense path walks 64-key tiles");
 
   // Each K/V slot is an LDS object of its own and the phase loop is unrolled
   // by two, so every slot a phase touches is a compile-time constant: the
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
       int c = a.count[r];
       c = c < 0 ? 0 : (c > a.cap ? a.cap : c);
       nb = c;
-      return (c + SPT - 1) / SPT;
+      return TPE > 1 ? c * TPE : (c + SPT - 1) / SPT;
     }
   };
   const int row = 2 * pair + half, orow = 2 * pair + (1 - half);
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   auto fetch = [&](Entry& E, int tile) {
     if constexpr (!DENSE) {
       const int last = nblk > 0 ? nblk - 1 : 0;
-      const int e = tile * SPT + lane % SPT;
+      const int e = TPE > 1 ? tile / TPE : tile * SPT + lane % SPT;
       const int ec = e < last ? e : last;
       E.blk = lidx[ec];
       E.w = PC ? lwc[(size_t)ec * a.C + ccl] : lw[ec];
@@ -177,14 +180,21 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
       t.bias = tile * 64 < a.L ? 0.f : -INFINITY;
       t.past = __ballot(tile * 64 < a.L && tile * 64 + lane >= a.L);
     } else {
-      const int e = tile * SPT + lane % SPT;
+      const int e = TPE > 1 ? tile / TPE : tile * SPT + lane % SPT;
       const bool ok = e < nblk && (unsigned)E.blk < (unsigned)a.NK;
-      const uint32_t bb = ok ? (uint32_t)E.blk * (BK * D * 2) : OOB;
+      // (a block of several tiles: this tile's 64 keys start sub * 64 keys into it)
+      const int sub = TPE > 1 ? tile % TPE : 0;
+      const uint32_t bb = ok ? (uint32_t)E.blk * (BK * D * 2) + (uint32_t)sub * (64 * D * 2) : OOB;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) base[j] = __builtin_amdgcn_readlane(bb, ((j * NW + wq) * KPI) / BK);
+      for (int j = 0; j < NCH; ++j)
+        base[j] = __builtin_amdgcn_readlane(bb, TPE > 1 ? 0 : ((j * NW + wq) * KPI) / BK);
       t.bias = ok ? __log2f(E.w) : -INFINITY;
       t.past = 0ull;
-      if (__ballot(ok && (E.blk + 1) * BK > a.L) != 0ull) {  // the block holding key L-1 (rare)
+      if constexpr (TPE > 1) {
+        // one entry for the whole tile, key k at block row sub * 64 + k
+        const int k0 = E.blk * BK + sub * 64;
+        if (__ballot(ok && k0 + 64 > a.L) != 0ull) t.past = __ballot(ok && k0 + lane >= a.L);
+      } else if (__ballot(ok && (E.blk + 1) * BK > a.L) != 0ull) {  // the block holding key L-1 (rare)
         // key k of the tile lies in entry k / BK, row k % BK
         int kb = 0;
         bool kok = false;
@@ -533,7 +543,8 @@ static hipError_t launch_pp_bk(const AttendLaunch& a, hipStream_t st, bool dense
   switch (a.Bk) {
     case 16: return launch_pp_t<D, 16, false>(a, st);
     case 32: return launch_pp_t<D, 32, false>(a, st);
-    default: return launch_pp_t<D, 64, false>(a, st);
+    case 64: return launch_pp_t<D, 64, false>(a, st);
+    default: return launch_pp_t<D, 128, false>(a, st);
   }
 }
 

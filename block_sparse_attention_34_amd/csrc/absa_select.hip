@@ -581,12 +581,14 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
 }
 
 // ============================================================================= K3
-// Sampling, one list per wave: the row's list (one list per row) or the list
-// of cluster j of a row (per-cluster lists: list row C + j, the full budget,
-// Philox counter word i C + j; a cluster without members gets an empty list).
-// Lane l holds the scores of four chunks of P contiguous blocks, those of the
-// threads l, l + 64, l + 128, l + 192 of a 256-thread layout that gives each
-// thread P blocks, in registers for the whole list:
+// Sampling: the row's list (one list per row) or the list of cluster j of a
+// row (per-cluster lists: list row C + j, the full budget, Philox counter word
+// i C + j; a cluster without members gets an empty list), held by WPL waves
+// (one for NK <= 5120, two up to 8192, four beyond).  The list's blocks are
+// laid out over 256 WPL layout threads of P contiguous blocks each (P a
+// multiple of 4, the smallest with 256 WPL P >= NK, and exactly the kernel's
+// compile-time chunk size); lane l of wave w holds the chunks of layout
+// threads 256 w + 64 v + l, v = 0..3, in registers for the whole list:
 //  * SIP capping rounds in straight-line code.  A block is free while its
 //    register holds a positive score; capping sets it to -0, which adds
 //    nothing to a sum, is never capped again and stays apart from a zero
@@ -597,42 +599,53 @@ __global__ __launch_bounds__(256, 2) void ibcs_logit_kernel(const uint16_t* __re
 //  * the decisions: probability (1 capped, s R / S_U other positive scores, 0
 //    else), one Philox block per 4 consecutive blocks, and the list entries
 //    in block order (thread-order prefix sums).
-// No LDS and no workgroup barrier: each wave owns its list.
-constexpr int SR_WAVES = 4;  // lists per workgroup
+// With one wave per list there is no LDS and no barrier (four lists per
+// workgroup).  With several, the workgroup is the list and every total and
+// prefix crosses the waves through LDS after a barrier; all of the list's
+// waves see the same totals, so they take the same branches and barriers.
+constexpr int SR_WAVES = 4;  // lists per workgroup with one wave per list
 
 __device__ __forceinline__ bool is_neg_zero(float x) { return __float_as_uint(x) == 0x80000000u; }
 
 constexpr int SR_SIP = 0, SR_TOPK = 1;
 
-template <int PM, int MODE>
-__global__ __launch_bounds__(64 * SR_WAVES) void sip_rows_kernel(SelectLaunch a, int nlists, int NKs) {
+// (at least three waves per SIMD: the kernel is bound by its vector work and
+// latency, and the 20-block chunks fit in the 168 registers that allows)
+template <int PM, int MODE, int WPL>
+__global__ __launch_bounds__(64 * (WPL == 1 ? SR_WAVES : WPL), 3) void sip_rows_kernel(SelectLaunch a, int nlists,
+                                                                                     int NKs) {
+  static_assert(PM % 4 == 0 && (WPL == 1 || WPL == 2 || WPL == 4), "chunk size and waves per list");
   const int lane = threadIdx.x & 63;
-  const int lst = blockIdx.x * SR_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (lst >= nlists) return;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lst = WPL == 1 ? blockIdx.x * SR_WAVES + wv : blockIdx.x;
+  const int wl = WPL == 1 ? 0 : wv;  // this wave's part of the list
+  if (lst >= nlists) return;         // (uniform over a list's waves)
   const int C = a.C;
   const int row = a.per_cluster ? lst / C : lst;
   const int jc = a.per_cluster ? lst - row * C : 0;
   const int bh = row / a.NQ, i = row - bh * a.NQ;
   const int NK = a.NK;
   if (a.per_cluster && a.nj[(size_t)row * C + jc] == 0) {
-    if (lane == 0) a.count[lst] = 0;
+    if (lane == 0 && wl == 0) a.count[lst] = 0;
     return;
   }
   const uint32_t ctr1 = a.per_cluster ? (uint32_t)(i * C + jc) : (uint32_t)i;
-  const int P = ((NK + 1023) >> 10) << 2;  // blocks per layout thread, <= PM
+  // blocks per layout thread: equal to PM (the launch picks the instance), but
+  // formed at run time, which keeps the chunk addressing as cheap in registers
+  const int P = 4 * ((NK + 1024 * WPL - 1) / (1024 * WPL));
   // The layout threads' chunks in registers.  The row holds NKs entries (a
   // multiple of 4, zero past NK) behind a buffer resource of that size: every
   // 16-byte piece lies wholly inside or wholly past its end, and the pieces
-  // past it read as 0, so chunk padding is 0 without a per-element test.
+  // past it read as 0, so chunk padding is 0 without a per-element test (and
+  // lies after every block: the chunks tile [0, 256 WPL P) exactly).
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(a.s + (size_t)lst * NKs), 0, NKs * 4, 0x00020000);
-  int b0[4], nb[4];
+  int b0[4];
   float sv[4][PM];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int bt = (64 * v + lane) * P;
-    b0[v] = min(NK, bt);
-    nb[v] = min(NK, b0[v] + P) - b0[v];
+    const int bt = (64 * (4 * wl + v) + lane) * P;
+    b0[v] = bt;
 #pragma unroll
     for (int e = 0; e < PM; e += 4) {
       const u32x4 x4 = __builtin_amdgcn_raw_buffer_load_b128(srs, (bt + e) * 4, 0, 0);
@@ -640,29 +653,71 @@ __global__ __launch_bounds__(64 * SR_WAVES) void sip_rows_kernel(SelectLaunch a,
       for (int q = 0; q < 4; ++q) sv[v][e + q] = __uint_as_float(x4[q]);
     }
   }
+  // Sums over the list's waves in wave order, through one of two LDS slots
+  // (alternating, so a wave that runs ahead to the next exchange cannot
+  // overwrite a slot another wave still reads: it must pass the barrier of
+  // the exchange in between first).
+  __shared__ float xf[2][WPL];
+  __shared__ int xi[2][WPL];
+  int xk = 0;
+  auto across = [&](float t) {
+    if constexpr (WPL == 1) {
+      return t;
+    } else {
+      if (lane == 0) xf[xk][wl] = t;
+      __syncthreads();
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPL; ++w) s += xf[xk][w];
+      xk ^= 1;
+      return s;
+    }
+  };
+  // (the int exchange also returns the sum of the waves before this one)
+  auto across_i = [&](int t, int& before) {
+    before = 0;
+    if constexpr (WPL == 1) {
+      return t;
+    } else {
+      if (lane == 0) xi[xk][wl] = t;
+      __syncthreads();
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < WPL; ++w) {
+        const int x = xi[xk][w];
+        before += w < wl ? x : 0;
+        s += x;
+      }
+      xk ^= 1;
+      return s;
+    }
+  };
   // totals in the layout's thread order
   auto total4 = [&](const float (&x)[4]) {
     float t = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) t += wave_total(x[v]);
-    return t;
+    return across(t);
   };
   auto total4i = [&](const int (&x)[4]) {
-    int t = 0;
+    int t = 0, before;
 #pragma unroll
     for (int v = 0; v < 4; ++v) t += wave_total_i(x[v]);
-    return t;
+    return across_i(t, before);
   };
   // exclusive prefix of per-thread counts in the layout's thread order, and the total
   auto scan4 = [&](const int (&x)[4], int (&off)[4]) {
-    int base = 0;
+    int base = 0, before;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int inc = wave_inclusive_scan(x[v], lane);
       off[v] = base + inc - x[v];
       base += __shfl(inc, 63, 64);
     }
-    return base;
+    const int total = across_i(base, before);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) off[v] += before;
+    return total;
   };
 
   uint64_t km[4] = {0ull, 0ull, 0ull, 0ull};  // kept blocks of each chunk
@@ -733,7 +788,8 @@ __global__ __launch_bounds__(64 * SR_WAVES) void sip_rows_kernel(SelectLaunch a,
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int e = 0; e < PM; ++e) c += (__float_as_uint(sv[v][e]) >= mid);
-      if (wave_total_i(c) >= a.kstar) lo = mid; else hi = mid;
+      int before;
+      if (across_i(wave_total_i(c), before) >= a.kstar) lo = mid; else hi = mid;
     }
     int gt[4], eq[4], rank[4];
 #pragma unroll
@@ -787,9 +843,9 @@ __global__ __launch_bounds__(64 * SR_WAVES) void sip_rows_kernel(SelectLaunch a,
     for (int v = 0; v < 4; ++v)
 #pragma unroll
       for (int e = 0; e < PM; ++e)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[v][e]), prs, ((64 * v + lane) * P + e) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[v][e]), prs, (b0[v] + e) * 4, 0, 0);
   }
-  if (lane == 0) a.count[lst] = total;
+  if (lane == 0 && wl == 0) a.count[lst] = total;
 }
 
 // Lists that keep every block with probability 1 (SIP with n* >= NK, top-k
@@ -959,21 +1015,38 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st, hipEvent_t* ev) 
     if (all || (a.mode == 1 && a.kstar <= 0)) {
       sel_all_kernel<<<nlists, 256, 0, st>>>(a, all ? 1 : 0);
     } else {
-      const dim3 grid((nlists + SR_WAVES - 1) / SR_WAVES);
-      const int P = ((a.NK + 1023) >> 10) << 2;
+      // waves per list: one up to 20 blocks per layout thread (80 score registers
+      // per lane), else two or four with at most 16 (the multi-wave kernel keeps
+      // a few more registers live); P is then exactly an instantiated chunk size
+      const int wpl = a.NK <= 5120 ? 1 : (a.NK <= 8192 ? 2 : 4);
+      const int P = 4 * ((a.NK + 1024 * wpl - 1) / (1024 * wpl));
       const bool sip = a.mode == 0;
-#define ABSA_SR(PP)                                                                     \
-  if (sip) sip_rows_kernel<PP, SR_SIP><<<grid, 64 * SR_WAVES, 0, st>>>(a, nlists, NKs); \
-  else sip_rows_kernel<PP, SR_TOPK><<<grid, 64 * SR_WAVES, 0, st>>>(a, nlists, NKs)
-      if (P <= 4) { ABSA_SR(4); }
-      else if (P <= 8) { ABSA_SR(8); }
-      else if (P <= 12) { ABSA_SR(12); }
-      else if (P <= 16) { ABSA_SR(16); }
-      else if (P <= 20) { ABSA_SR(20); }
-      else if (P <= 24) { ABSA_SR(24); }
-      else if (P <= 32) { ABSA_SR(32); }
-      else if (P <= 40) { ABSA_SR(40); }
-      else { ABSA_SR(48); }  // NK <= 12288
+#define ABSA_SR(PP, WW)                                                                                   \
+  do {                                                                                                    \
+    const dim3 grid(WW == 1 ? (nlists + SR_WAVES - 1) / SR_WAVES : nlists);                               \
+    const int nt = 64 * (WW == 1 ? SR_WAVES : WW);                                                        \
+    if (sip) sip_rows_kernel<PP, SR_SIP, WW><<<grid, nt, 0, st>>>(a, nlists, NKs);                        \
+    else sip_rows_kernel<PP, SR_TOPK, WW><<<grid, nt, 0, st>>>(a, nlists, NKs);                           \
+  } while (0)
+      if (wpl == 1) {
+        switch (P) {
+          case 4: ABSA_SR(4, 1); break;
+          case 8: ABSA_SR(8, 1); break;
+          case 12: ABSA_SR(12, 1); break;
+          case 16: ABSA_SR(16, 1); break;
+          case 20: ABSA_SR(20, 1); break;
+          default: return hipErrorInvalidValue;
+        }
+      } else if (wpl == 2) {  // 5120 < NK <= 8192
+        switch (P) {
+          case 12: ABSA_SR(12, 2); break;
+          case 16: ABSA_SR(16, 2); break;
+          default: return hipErrorInvalidValue;
+        }
+      } else {  // 8192 < NK <= 12288
+        if (P != 12) return hipErrorInvalidValue;
+        ABSA_SR(12, 4);
+      }
 #undef ABSA_SR
     }
     hipError_t e = hipGetLastError();

@@ -93,7 +93,7 @@ typedef struct absa_problem {
   int32_t B, H, L, d;        /* d in {64, 128}                                 */
   int32_t T, Hs, Ws;         /* token grid; T*Hs*Ws must equal L               */
   int32_t q_block;           /* Bq in {64, 128}                                */
-  int32_t kv_block;          /* Bk in {16, 32, 64}                             */
+  int32_t kv_block;          /* Bk in {16, 32, 64, 128}                        */
   float scale;               /* softmax scale sigma; <= 0 selects 1/sqrt(d)    */
   int32_t out_bf16;          /* 0: O is fp32, 1: O is bf16                      */
 } absa_problem;
@@ -126,10 +126,15 @@ int32_t absa_version(void);
 /* Static text for a status code; never NULL. */
 const char* absa_status_string(int32_t status);
 
-/* NQ = ceil(L/Bq) and NK = ceil(L/Bk) for a valid problem ([host] pointers). */
+/* NQ = ceil(L/Bq) and NK = ceil(L/Bk) for a valid problem ([host] pointers).
+ * Passage: AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği", IBCS item (query
+ * blocks are formed without permuting tokens, so blocks are contiguous token
+ * ranges of the clip's own order). */
 absa_status absa_num_blocks(const absa_problem* prob, int32_t* nq, int32_t* nk);
 
-/* Bytes of device workspace absa_select needs ([host] pointers). */
+/* Bytes of device workspace absa_select needs ([host] pointers): the IBCS
+ * intermediates (block means, centroids, scores) of AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği",
+ * IBCS item. */
 absa_status absa_select_workspace(const absa_problem* prob, const absa_select_params* params,
                                   size_t* bytes);
 
@@ -143,7 +148,7 @@ absa_status absa_select_workspace(const absa_problem* prob, const absa_select_pa
  *               chip and never stored
  * mu, n_j and s are written by every call; kbar^T only by calls with a
  * non-NULL pi_out (the inspection mode), since the lists do not need it.
- * ([host] pointers; offsets has 5 entries). */
+ * ([host] pointers; offsets has 5 entries).  Passage: as absa_select. */
 absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_select_params* params,
                                          size_t* offsets);
 
@@ -152,7 +157,12 @@ absa_status absa_select_workspace_layout(const absa_problem* prob, const absa_se
  * the fp32 inclusion probability of every block, [rows][NK] (SIP: pi_b;
  * TOPK: 1 for kept, 0 otherwise; ALL: 1).  Requires NK <= 12288.
  * workspace: device memory of at least absa_select_workspace() bytes, 256-byte
- * aligned, owned by the caller, contents on entry ignored. */
+ * aligned, owned by the caller, contents on entry ignored.
+ * Passages: AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği",
+ * IBCS item (scores from clusters of each query block) and SIP item (blocks
+ * sampled in proportion to those scores, weight 1/pi); TOPK is the truncation
+ * of the same page's section "Video Difüzyon Modellerinde Dikkat (Attention)
+ * Darboğazı" (pruned blocks leave the softmax), ALL its dense attention. */
 absa_status absa_select(const absa_problem* prob, const absa_select_params* params, const void* q,
                         const void* k, const absa_blocklist* out, float* pi_out, void* workspace,
                         size_t workspace_bytes, void* stream);
@@ -179,7 +189,8 @@ absa_status absa_select_noalloc(const absa_problem* prob, const absa_select_para
  * order, written to the first min(n_ms, 5) entries of kernel_ms ([host]).  The
  * call waits for the selection to finish; the lists are those absa_select
  * gives.  Arguments and errors as absa_select; n_ms < 0 or a NULL kernel_ms
- * is ABSA_ERR_INVALID_ARG, a failed event call ABSA_ERR_HIP. */
+ * is ABSA_ERR_INVALID_ARG, a failed event call ABSA_ERR_HIP.  Passage: as
+ * absa_select. */
 absa_status absa_select_profile(const absa_problem* prob, const absa_select_params* params, const void* q,
                                 const void* k, const absa_blocklist* out, void* workspace, size_t workspace_bytes,
                                 void* stream, float* kernel_ms, int32_t n_ms);
@@ -187,11 +198,20 @@ absa_status absa_select_profile(const absa_problem* prob, const absa_select_para
 /* Block-sparse attention over given lists (the estimate above): for every
  * valid query of row r, attends to the keys of the blocks listed for r with
  * their weights.  o is [B, H, L, d] (fp32, or bf16 if out_bf16), 16-byte
- * aligned; only valid query rows are written.  `lists` is a [host] struct. */
+ * aligned; only valid query rows are written.  `lists` is a [host] struct.
+ * Passages: AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği",
+ * SIP item (the 1/pi weights enter the softmax numerator and denominator, one
+ * pass estimates dense attention) and kernel item (KV blocks much smaller than
+ * a tile are packed into full matrix-core tiles); the attention formula of the
+ * Cross-Attention glossary page's opening section. */
 absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, const void* v,
                         const absa_blocklist* lists, void* o, void* stream);
 
-/* Dense attention softmax(scale Q K^T) V over all L keys, same layouts. */
+/* Dense attention softmax(scale Q K^T) V over all L keys, same layouts.
+ * Passages: the 3D full attention of the AB-Attention page's section "Video
+ * Difüzyon Modellerinde Dikkat (Attention) Darboğazı" (the quantity the
+ * estimate approximates), written as in the Cross-Attention glossary page's
+ * opening section. */
 absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
                        void* stream);
 
@@ -221,20 +241,24 @@ typedef struct absa_cluster_lists {
   int32_t clusters; /* C; must equal the selection's cluster count                       */
 } absa_cluster_lists;
 
-/* Bytes of device workspace absa_select_clusters needs ([host] pointers). */
+/* Bytes of device workspace absa_select_clusters needs ([host] pointers).
+ * Passage: the PIVOT page, section "PIVOT'un arkasındaki iki gözlem". */
 absa_status absa_select_clusters_workspace(const absa_problem* prob, const absa_select_params* params,
                                            size_t* bytes);
 
 /* Per-cluster selection into `out` ([host] struct, device arrays, 4-byte
  * aligned).  Same requirements and workspace rules as absa_select (NK <=
- * 12288); the workspace is larger (scores and lists of every cluster). */
+ * 12288); the workspace is larger (scores and lists of every cluster).
+ * Passages: the PIVOT page, section "PIVOT'un arkasındaki iki gözlem" (one
+ * proxy per query group, its candidates refined per member), with the IBCS
+ * clusters and SIP draws of AB-Attention page, section "AB-Attention ve Üç Temel Yeniliği". */
 absa_status absa_select_clusters(const absa_problem* prob, const absa_select_params* params, const void* q,
                                  const void* k, const absa_cluster_lists* out, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
 /* Attention over per-cluster lists: query t of row r over the blocks its
  * cluster drew, with that cluster's weights.  Layouts as for absa_attend;
- * requires Bq = 128. */
+ * requires Bq = 128.  Passages: as absa_select_clusters and absa_attend. */
 absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const void* k, const void* v,
                                  const absa_cluster_lists* lists, void* o, void* stream);
 
@@ -293,13 +317,16 @@ typedef struct absa_fp8_operands {
   int32_t qk_int8; /* 0: q8/k8 hold E4M3 codes; 1: INT8 codes (QK below)          */
 } absa_fp8_operands;
 
-/* Bytes of device workspace absa_quantize_fp8 needs ([host] pointers). */
+/* Bytes of device workspace absa_quantize_fp8 needs ([host] pointers).
+ * Passage: VC-Attention page, section "İki darboğaz". */
 absa_status absa_fp8_workspace(const absa_problem* prob, size_t* bytes);
 
 /* Quantises bf16 Q, K, V ([B,H,L,128]) into `out` ([host] struct, device
  * arrays) by the rules above.  workspace: at least absa_fp8_workspace() bytes,
  * 256-byte aligned, contents on entry ignored.  Returns ABSA_ERR_UNSUPPORTED
- * unless d = 128 and Bk = 16. */
+ * unless d = 128 and Bk = 16.  Passage: VC-Attention page, section "İki
+ * darboğaz" (the value term's error, the per-block mean of V removed before
+ * quantising). */
 absa_status absa_quantize_fp8(const absa_problem* prob, const void* q, const void* k, const void* v,
                               const absa_fp8_operands* out, void* workspace, size_t workspace_bytes,
                               void* stream);
@@ -308,7 +335,9 @@ absa_status absa_quantize_fp8(const absa_problem* prob, const void* q, const voi
  * the blocks listed for each row (same list format as absa_attend); with
  * lists == NULL every key is kept with weight 1 (dense attention in FP8).
  * o as for absa_attend.  Returns ABSA_ERR_UNSUPPORTED unless d = 128,
- * Bq = 128 and Bk = 16. */
+ * Bq = 128 and Bk = 16.  Passages: VC-Attention page, section "İki darboğaz"
+ * (probabilities written as E4M3 bytes by one fused multiply-add) and section
+ * "Ölçümler" (composes with sparse attention). */
 absa_status absa_attend_fp8(const absa_problem* prob, const absa_fp8_operands* ops,
                             const absa_blocklist* lists, void* o, void* stream);
 

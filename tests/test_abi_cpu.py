@@ -102,7 +102,7 @@ def test_num_blocks_and_shape_errors(lib):
     assert lib.absa_num_blocks(ctypes.byref(prob(L=0)), ctypes.byref(nq), ctypes.byref(nk)) == _lib.ABSA_ERR_SHAPE
     assert lib.absa_num_blocks(None, ctypes.byref(nq), ctypes.byref(nk)) == _lib.ABSA_ERR_INVALID_ARG
     assert lib.absa_num_blocks(ctypes.byref(prob()), None, ctypes.byref(nk)) == _lib.ABSA_ERR_INVALID_ARG
-    for bad in (dict(d=96), dict(q_block=32), dict(kv_block=8), dict(kv_block=128)):
+    for bad in (dict(d=96), dict(q_block=32), dict(kv_block=8), dict(kv_block=256)):
         assert lib.absa_num_blocks(ctypes.byref(prob(**bad)), ctypes.byref(nq), ctypes.byref(nk)) == \
             _lib.ABSA_ERR_UNSUPPORTED
     assert lib.absa_num_blocks(ctypes.byref(prob(scale=float("nan"))), ctypes.byref(nq), ctypes.byref(nk)) == \

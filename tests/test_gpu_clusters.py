@@ -34,12 +34,12 @@ def absa():
     return m
 
 
-def _workload(H, T, Hs, Ws, d, seed, outliers=False):
+def _workload(H, T, Hs, Ws, d, seed, outliers=False, Bk=16):
     q, k, v = gen_fourier_heads(T, Hs, Ws, d, 4, 0.3, outliers, seed, list(range(H)))
     L = T * Hs * Ws
     sh = (1, H, L, d)
     return Workload(q=bf16_round(q.reshape(sh)), k=bf16_round(k.reshape(sh)), v=bf16_round(v.reshape(sh)),
-                    B=1, H=H, L=L, d=d, T=T, Hs=Hs, Ws=Ws, q_block=128, kv_block=16, keep=0.25)
+                    B=1, H=H, L=L, d=d, T=T, Hs=Hs, Ws=Ws, q_block=128, kv_block=Bk, keep=0.25)
 
 
 def _host(lists):
@@ -99,7 +99,7 @@ def _check(absa, wl, keep, C, rows=None, tag="", seed=0):
     o = o.cpu().numpy()
     count, kv, W, lab = _host(lists)
     rows = list(range(p.rows)) if rows is None else rows
-    res = O.select_clusters(wl.q, wl.k, 128, 16, keep32(keep), C=C, seed=seed, rows=rows)
+    res = O.select_clusters(wl.q, wl.k, 128, wl.kv_block, keep32(keep), C=C, seed=seed, rows=rows)
     diff = tot = 0
     got, ref = [], []
     for r_i, r in enumerate(rows):
@@ -114,7 +114,7 @@ def _check(absa, wl, keep, C, rows=None, tag="", seed=0):
             oo[res.lists[r_i][j][0]] = True
             diff += int((g ^ oo).sum())
             tot += p.nk
-        ref.append(O.attend_row_clusters(wl.q, wl.k, wl.v, bh, i, 128, 16, lab[r, :n].astype(np.int64), per,
+        ref.append(O.attend_row_clusters(wl.q, wl.k, wl.v, bh, i, 128, wl.kv_block, lab[r, :n].astype(np.int64), per,
                                          p.sigma))
         got.append(o[0, bh, i * 128: i * 128 + n])
     agree = 1.0 - diff / tot
@@ -130,10 +130,11 @@ def _check(absa, wl, keep, C, rows=None, tag="", seed=0):
         assert ((W[r, :c] == 0) | (W[r, :c] >= 1)).all() and (W[r, :c].max(axis=1) >= 1).all()
 
 
-@pytest.mark.parametrize("d,C", [(128, 4), (64, 2), (128, 8)])
-def test_cluster_attend_matches_oracle(absa, d, C):
-    wl = _workload(2, 3, 16, 21, d, seed=43)   # L = 1008: ragged query and KV tails
-    _check(absa, wl, 0.25, C, tag=f"clusters d={d} C={C}")
+@pytest.mark.parametrize("d,C,Bk", [(128, 4, 16), (64, 2, 16), (128, 8, 16), (128, 4, 32), (128, 4, 64),
+                                    (128, 4, 128), (64, 2, 128)])
+def test_cluster_attend_matches_oracle(absa, d, C, Bk):
+    wl = _workload(2, 3, 16, 21, d, seed=43, Bk=Bk)   # L = 1008: ragged query and KV tails
+    _check(absa, wl, 0.25, C, tag=f"clusters d={d} C={C} Bk={Bk}")
 
 
 def test_cluster_empty_cluster_rows(absa):

@@ -206,6 +206,17 @@ def test_block_size_variants(absa, d, Bq, Bk):
     _check_selection_and_attend(absa, wl, 0.15, Bk=Bk, tag=f"d{d} Bq{Bq} Bk{Bk}")
 
 
+@pytest.mark.parametrize("d,Bq", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("grid", [(5, 15, 16), (5, 15, 13)])
+def test_tile_sized_blocks(absa, d, Bq, grid):
+    # 128-key blocks, two 64-key tiles each: L = 1200 ends 48 keys into the last
+    # block (its second tile lies wholly past L), L = 975 ends 79 keys into it
+    # (the tail falls in the second tile)
+    wl = _random_workload(2, *grid, d, Bq, 128, seed=23 + grid[2], modes=8)
+    for mode in (O.SEL_SIP, O.SEL_TOPK, O.SEL_ALL):
+        _check_selection_and_attend(absa, wl, 0.3, Bk=128, mode=mode, tag=f"d{d} Bq{Bq} Bk128 L={wl.L} mode {mode}")
+
+
 @pytest.mark.parametrize("mode", [O.SEL_TOPK, O.SEL_ALL])
 def test_topk_and_all_modes(absa, mode):
     wl = _random_workload(2, 5, 15, 16, 128, 128, 16, seed=4, modes=8)

@@ -114,12 +114,14 @@ def test_select_knobs_wan14b_720p(absa, C, Tk, mode):
     _check(absa, wl, 0.095, rows, C, Tk, mode, tag="Wan2.1-14B 720p")
 
 
-def test_prior_art_arm_wan14b_720p(absa):
-    # one mean query per query block (C = 1), top-k truncation, 64-key (tile-sized) KV blocks
+@pytest.mark.parametrize("Bk", [64, 128])
+def test_prior_art_arm_wan14b_720p(absa, Bk):
+    # one mean query per query block (C = 1), top-k truncation, KV blocks of one
+    # 64-key tile or of a whole 128 x 128 tile
     wl = _wan14b()
-    p = problem(wl, kv_block=64)
+    p = problem(wl, kv_block=Bk)
     rows = sample_rows(p.nq, wl.H, 24, seed=321)
-    _check(absa, wl, 0.10, rows, 1, 3, O.SEL_TOPK, Bk=64, tag="prior-art arm 720p")
+    _check(absa, wl, 0.10, rows, 1, 3, O.SEL_TOPK, Bk=Bk, tag="prior-art arm 720p")
 
 
 # ----------------------------------------------------------------------------- dense at the 720p shape
@@ -183,3 +185,70 @@ def test_sip_seed_average_matches_exact_expectation(absa):
         _say(f"row {r}: max |mean - E[o]| {dev_.max():.3e}, sd of the mean {sd.mean():.3e}, max z {z.max():.2f}, "
              f"rms z {np.sqrt((z ** 2).mean()):.2f}")
         assert np.all(dev_ <= 6.0 * sd + 1e-2)
+
+
+# ----------------------------------------------------------------------------- sampler at large NK
+
+@pytest.mark.parametrize("grid", [(16, 40, 150), (14, 40, 200), (18, 40, 200), (22, 40, 200)])
+def test_sampler_large_block_counts(absa, grid):
+    """NK = 6000, 7000 (two waves per list, 12- and 16-block chunks), 9000 and 11000 (four waves,
+    12-block chunks) at Bk = 16.  On sampled rows, given the scores the selection wrote to its
+    workspace, the lists follow the sampling definition exactly: top-k keeps the k* highest scores
+    (ties to the lower index); SIP keeps b iff u_b < pi_b for the oracle's Philox uniforms and the
+    kernel's fp32 pi, with weights fp32(1 / pi), and pi equals the oracle's capping of the same
+    scores to the fp32 rounding of its sums.  Decisions also agree with the oracle's own selection,
+    and the outputs with the oracle fed the GPU's lists."""
+    import torch
+    T, Hs, Ws = grid
+    q, k, v = (bf16_round(x) for x in gen_fourier_heads(T, Hs, Ws, 128, 8, 0.3, False, 60 + T, [0, 1]))
+    L = T * Hs * Ws
+    sh = (1, 2, L, 128)
+    wl = Workload(q=q.reshape(sh), k=k.reshape(sh), v=v.reshape(sh), B=1, H=2, L=L, d=128, T=T, Hs=Hs, Ws=Ws,
+                  q_block=128, kv_block=16, keep=0.08)
+    p = problem(wl)
+    NK = p.nk
+    NKs = -(-NK // 4) * 4
+    keep = 0.08
+    n_star = keep32(keep) * NK
+    rows = sample_rows(p.nq, wl.H, 12, seed=70 + T)
+    qd, kd, vd = dev(wl.q), dev(wl.k), dev(wl.v)
+    for mode in (O.SEL_SIP, O.SEL_TOPK):
+        seed, stream_id = 17, 2
+        lists, pi, ws = absa.select(p, qd, kd, keep, seed=seed, stream_id=stream_id, mode=mode, want_pi=True)
+        o = absa.attend(p, qd, kd, vd, lists)
+        torch.cuda.synchronize()
+        count, kv, w = lists_to_host(lists)
+        pi = pi.cpu().numpy()
+        offs = absa.workspace_layout(p, keep, mode=mode)
+        s_all = ws.cpu().numpy()[offs[3]: offs[3] + p.rows * NKs * 4].view(np.float32).reshape(p.rows, NKs)
+        assert not s_all[:, NK:].any()
+        max_rel = 0.0
+        for r in rows:
+            bh, i = divmod(int(r), p.nq)
+            s = s_all[r, :NK].astype(np.float64)
+            got = kv[r, :count[r]]
+            if mode == O.SEL_TOPK:
+                ref, _, _ = O.select_row(s, n_star, O.SEL_TOPK, seed, stream_id, bh, i)
+                np.testing.assert_array_equal(got, ref)
+                assert (w[r, :count[r]] == 1.0).all()
+                np.testing.assert_array_equal(np.nonzero(pi[r])[0], ref)
+            else:
+                u = O.sip_uniforms(seed, stream_id, bh, i, NK)
+                np.testing.assert_array_equal(got, np.nonzero(u < pi[r].astype(np.float64))[0])
+                inv = (np.float32(1.0) / pi[r, got]).astype(np.float32)
+                np.testing.assert_array_equal(w[r, :count[r]].view(np.uint32), inv.view(np.uint32))
+                ref_pi = O.sip_inclusion(s, n_star)
+                rel = np.abs(pi[r] - ref_pi) / np.maximum(ref_pi, 1e-30)
+                max_rel = max(max_rel, float(rel[ref_pi > 0].max()))
+                assert ((pi[r] > 0) == (ref_pi > 0)).all()
+                assert rel[ref_pi > 0].max() <= 1e-4
+        res = O.select(wl.q, wl.k, 128, 16, keep32(keep), seed=seed, stream=stream_id, mode=mode, rows=rows)
+        agree = decision_agreement(count, kv, res, NK)
+        ref_o = oracle_rows_from_gpu_lists(wl, 128, 16, count, kv, w, rows, p.sigma)
+        g = gpu_rows(o.cpu().numpy(), wl, 128, rows)
+        err = assert_close(np.concatenate([g[r] for r in rows]), np.concatenate([ref_o[r] for r in rows]),
+                           f"NK={NK} mode {mode}")
+        _say(f"NK={NK} mode {mode}: rows={len(rows)} lists follow the definition on the kernel's scores "
+             f"(max rel pi diff {max_rel:.2e}), agreement={agree:.6f} max_abs={err[0]:.3e} rel_l2={err[1]:.3e} "
+             f"mean_count={count.mean():.1f}")
+        assert agree >= AGREE
