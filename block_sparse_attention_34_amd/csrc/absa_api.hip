@@ -398,7 +398,7 @@ absa_status absa_select_profile(const absa_problem* prob, const absa_select_para
   if (e == hipSuccess) e = hipEventSynchronize(ev[absa::kSelectEvents - 1]);
   for (int i = 0; e == hipSuccess && i + 1 < absa::kSelectEvents && i < n_ms; ++i)
     e = hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]);
-  for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);  // (a failure here changes no result)
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
 
