@@ -226,17 +226,27 @@ def attend_source_digest():
     return h.hexdigest()[:16]
 
 
+def workload_tag(config, kv_block, keep):
+    """Name of a workload's committed profiles: the default (Wan2.1-14B 720p, Bk 16, keep 9.5%)
+    is "wan14b_720p", the others add the block size (if not 16) and the budget in percent."""
+    base = {2: "wan13b_480p", 3: "wan14b_720p", 4: "hunyuan_720p"}[config]
+    if config == 3 and kv_block == 16 and abs(keep - 0.095) < 1e-9:
+        return base
+    return base + (f"_bk{kv_block}" if kv_block != 16 else "") + f"_keep{keep * 100:g}"
+
+
 def measured_traffic(workload_tag="wan14b_720p"):
-    """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if
-    it was taken on the current kernel source (else None: the kernel changed since)."""
-    prof = os.path.join(ROOT, "profiles", f"attend_kernel_{workload_tag}_traffic.md")
-    try:
-        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line
-                      and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "attend_source_sha256_16"))
-        if fields.get("attend_source_sha256_16") == attend_source_digest():
-            return int(fields["traffic_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
-        pass
+    """HBM bytes per attend launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary of
+    the workload, if it was taken on the current kernel source (else None: the kernel changed since)."""
+    for stem in ("attend_kernel", "attend_select_kernels"):
+        prof = os.path.join(ROOT, "profiles", f"{stem}_{workload_tag}_traffic.md")
+        try:
+            fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines() if ": " in line
+                          and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "attend_source_sha256_16"))
+            if fields.get("attend_source_sha256_16") == attend_source_digest():
+                return int(fields["traffic_bytes_per_launch"])
+        except (OSError, ValueError, KeyError):
+            pass
     return None
 
 
@@ -401,8 +411,8 @@ def main():
                    "selection": "IBCS + SIP", "seed": 0},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic() if (args.config == 3 and Bk == 16 and p.H == 40 and
-                                                       abs(args.keep - 0.095) < 1e-9) else None},
+                     "traffic": measured_traffic(workload_tag(args.config, Bk, args.keep))
+                     if not args.heads else None},
         "attend_ms": att_avg,
         "select_ms": sel_avg,
         "attend_dense_equiv_tflops": dense_flops / (att_avg * 1e-3) / 1e12,

@@ -36,3 +36,20 @@ def test_traffic_is_reported_only_for_the_source_it_was_measured_on(tmp_path, mo
     f.write_text(f"traffic_bytes_per_launch: 123\nattend_source_sha256_16: {digest}\n")
     assert bench.measured_traffic("t") is None
     assert bench.measured_traffic("missing") is None
+
+
+def test_workload_tags_name_the_committed_profiles():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.workload_tag(3, 16, 0.095) == "wan14b_720p"
+    assert bench.workload_tag(3, 16, 0.08) == "wan14b_720p_keep8"
+    assert bench.workload_tag(3, 16, 0.11) == "wan14b_720p_keep11"
+    assert bench.workload_tag(2, 16, 0.10) == "wan13b_480p_keep10"
+    assert bench.workload_tag(4, 32, 0.08) == "hunyuan_720p_bk32_keep8"
+    # a summary under the combined selection + attention name is found as well
+    tag = bench.workload_tag(4, 16, 0.08)
+    assert tag == "hunyuan_720p_keep8"
+    path = os.path.join(ROOT, "profiles", f"attend_select_kernels_{tag}_traffic.md")
+    if os.path.exists(path):
+        v = bench.measured_traffic(tag)
+        assert v is None or v > 0
