@@ -337,14 +337,23 @@ def main():
     o = torch.empty((p.B, p.H, p.L, p.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(absa.select_workspace_bytes(p, args.keep), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # 64-query blocks: adjacent blocks share one 128-query row of the two-row kernel (absa_attend_pairs)
+    pairs = p.q_block == 64
+    pws = torch.empty(absa.attend_pairs_workspace_bytes(p), dtype=torch.uint8, device="cuda") if pairs else None
+
+    def attend(lst, out):
+        if pairs:
+            absa.attend_pairs(p, q, k, v, lst, out=out, workspace=pws)
+        else:
+            absa.attend(p, q, k, v, lst, out=out)
 
     def step():
         absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
-        absa.attend(p, q, k, v, lists, out=o)
+        attend(lists, o)
 
     if args.kernels_once:
         step()
-        absa.attend(p, q, k, v, lists, out=o)
+        attend(lists, o)
         absa.dense(p, q, k, v, out=o)
         torch.cuda.synchronize()
         print("[bench] kernels-once done", file=sys.stderr, flush=True)
@@ -362,7 +371,7 @@ def main():
         ev[s][0].record(stream)
         absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
         ev[s][1].record(stream)
-        absa.attend(p, q, k, v, lists, out=o)
+        attend(lists, o)
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -383,11 +392,16 @@ def main():
     nk_valid = torch.clamp(L - blk * Bk, max=Bk).double() * mask
     kept_keys = nk_valid.sum(dim=1)
     alg_flops = float((4.0 * nq_valid * d * kept_keys).sum())
-    # the attention kernel runs rows 2p and 2p + 1 together, max(T, T') 64-key steps each
-    tiles = (count * Bk + 63) // 64
+    # the attention kernel runs 128-query rows 2p and 2p + 1 together, max(T, T') 64-key steps
+    # each (with 64-query blocks, the rows are the pairs' union lists the timed calls left)
+    if pairs:
+        rows128 = p.B * p.H * (-(-L // 128))
+        tiles = (pws[: rows128 * 4].view(torch.int32).long() * Bk + 63) // 64
+    else:
+        tiles = (count * Bk + 63) // 64
     tp = torch.nn.functional.pad(tiles, (0, tiles.numel() % 2)).view(-1, 2)
     exec_tiles = 2.0 * float(tp.max(dim=1).values.double().sum())
-    exec_flops = 4.0 * Bq * 64 * d * exec_tiles
+    exec_flops = 4.0 * 128 * 64 * d * exec_tiles
     alg_bytes = float(kept_keys.sum()) * 4 * d  # K + V bf16 gathered per kept key
     dense_flops = 4.0 * p.B * p.H * float(L) ** 2 * d
     att_avg = sum(att_ms) / len(att_ms)
@@ -408,7 +422,8 @@ def main():
         "data": "synthetic (seeded Fourier-mode Q/K with outlier tokens, N(0,1) V)",
         "config": {"workload": wl.name, "B": p.B, "H": p.H, "L": L, "d": d, "grid": [wl.T, wl.Hs, wl.Ws],
                    "q_block": Bq, "kv_block": Bk, "keep": args.keep, "clusters": 4, "kmeans_steps": 3,
-                   "selection": "IBCS + SIP", "seed": 0},
+                   "selection": "IBCS + SIP", "seed": 0,
+                   "attend": "pairs of 64-query blocks" if pairs else "two-row kernel"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(workload_tag(args.config, Bk, args.keep))
@@ -450,7 +465,7 @@ def main():
     o_tk = torch.empty_like(o)
     lists_tk = absa.alloc_lists(p)
     absa.select(p, q, k, args.keep, seed=0, mode="topk", lists=lists_tk, workspace=ws)
-    absa.attend(p, q, k, v, lists_tk, out=o_tk)
+    attend(lists_tk, o_tk)
     line["rel_l2_vs_dense"] = {"sip": float(torch.linalg.vector_norm(o - o_dense)) / ref_norm,
                                "topk": float(torch.linalg.vector_norm(o_tk - o_dense)) / ref_norm}
     del o_dense, o_tk, lists_tk

@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
 
 __all__ = [
-    "Problem", "BlockLists", "select", "select_noalloc", "select_profile", "SELECT_KERNELS", "attend", "dense", "num_blocks", "select_workspace_bytes",
+    "Problem", "BlockLists", "select", "select_noalloc", "select_profile", "SELECT_KERNELS", "attend", "attend_pairs",
+    "attend_pairs_workspace_bytes", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
     "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
     "ClusterLists", "alloc_cluster_lists", "select_clusters_workspace_bytes", "select_clusters", "attend_clusters",
@@ -251,6 +252,36 @@ def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):
     st = library().absa_attend(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
                                out.data_ptr(), _stream())
     _lib.check(st, "absa_attend")
+    return out
+
+
+def attend_pairs_workspace_bytes(prob: Problem) -> int:
+    """Bytes of workspace ``attend_pairs`` needs (64-query blocks)."""
+    n = ctypes.c_size_t()
+    p = prob.c()
+    _lib.check(library().absa_attend_pairs_workspace(ctypes.byref(p), ctypes.byref(n)), "absa_attend_pairs_workspace")
+    return int(n.value)
+
+
+def attend_pairs(prob: Problem, q, k, v, lists: BlockLists, out=None, workspace=None):
+    """``attend`` for 64-query blocks through absa_attend_pairs: adjacent query blocks share one
+    128-query row of the two-row kernel over the union of their lists.  Returns O [B,H,L,d]."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    _check_lists(prob, lists, q.device, need_cap_nk=False)
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    else:
+        _check_out(prob, out, q.device)
+    nbytes = attend_pairs_workspace_bytes(prob)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p = prob.c()
+    bl = lists.c()
+    st = library().absa_attend_pairs(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
+                                     out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    _lib.check(st, "absa_attend_pairs")
     return out
 
 

@@ -548,6 +548,103 @@ absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const 
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
 
+// Pairs of 64-query blocks: the union lists [rows128] count, [rows128][NK] indices
+// and [rows128][NK][2] weights, 256-byte aligned regions.
+struct PairWs {
+  size_t ucount, uidx, uw, total;
+};
+static PairWs pair_ws(const absa_problem* p, const Dims& dm) {
+  const int64_t NQo = (p->L + 127) / 128;
+  const int64_t rows = dm.BH * NQo;
+  PairWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.ucount = take((size_t)rows * 4);
+  w.uidx = take((size_t)rows * dm.NK * 4);
+  w.uw = take((size_t)rows * dm.NK * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+static absa_status check_pairs_problem(const absa_problem* prob, Dims* dm) {
+  absa_status st = check_problem(prob, dm);
+  if (st != ABSA_OK) return st;
+  if (prob->q_block != 64) return ABSA_ERR_UNSUPPORTED;
+  if (!head_fits_buffer(prob)) return ABSA_ERR_UNSUPPORTED;
+  if (dm->NK > kMaxNK) return ABSA_ERR_UNSUPPORTED;  // the union keeps a word per block in LDS
+  return ABSA_OK;
+}
+
+absa_status absa_attend_pairs_workspace(const absa_problem* prob, size_t* bytes) {
+  if (!bytes) return ABSA_ERR_INVALID_ARG;
+  Dims dm;
+  absa_status st = check_pairs_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  *bytes = pair_ws(prob, dm).total;
+  return ABSA_OK;
+}
+
+absa_status absa_attend_pairs(const absa_problem* prob, const void* q, const void* k, const void* v,
+                              const absa_blocklist* lists, void* o, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Dims dm;
+  absa_status st = check_pairs_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  if (!q || !k || !v || !o) return ABSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ABSA_ERR_ALIGNMENT;
+  st = check_lists(lists, false, dm.NK);
+  if (st != ABSA_OK) return st;
+  const PairWs w = pair_ws(prob, dm);
+  if (!workspace || workspace_bytes < w.total) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return ABSA_ERR_ALIGNMENT;
+  char* ws = static_cast<char*>(workspace);
+  const int NQo = (prob->L + 127) / 128;
+  absa::PairUnionLaunch u{};
+  u.count = lists->count;
+  u.kv_idx = lists->kv_idx;
+  u.inv_pi = lists->inv_pi;
+  u.cap = lists->cap;
+  u.NK = dm.NK;
+  u.NQi = dm.NQ;
+  u.NQo = NQo;
+  u.rows_out = (int)(dm.BH * NQo);
+  u.ucount = reinterpret_cast<int32_t*>(ws + w.ucount);
+  u.uidx = reinterpret_cast<int32_t*>(ws + w.uidx);
+  u.uw = reinterpret_cast<float*>(ws + w.uw);
+  u.ucap = dm.NK;
+  hipError_t e = absa::launch_pair_union(u, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return ABSA_ERR_HIP;
+  // the pairs as the rows of a 128-query problem, each query over its own block's list
+  absa::AttendLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.L = prob->L;
+  a.d = prob->d;
+  a.Bq = 128;
+  a.Bk = prob->kv_block;
+  a.NQ = NQo;
+  a.NK = dm.NK;
+  a.rows = u.rows_out;
+  a.out_bf16 = prob->out_bf16;
+  const float scale = prob->scale > 0.f ? prob->scale : 1.0f / std::sqrt((float)prob->d);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.count = u.ucount;
+  a.kv_idx = u.uidx;
+  a.inv_pi = nullptr;
+  a.cap = u.ucap;
+  a.wc = u.uw;
+  a.label = nullptr;
+  a.C = 2;
+  e = absa::launch_attend(a, static_cast<hipStream_t>(stream), false);
+  return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
+}
+
 absa_status absa_fp8_workspace(const absa_problem* prob, size_t* bytes) {
   if (!bytes) return ABSA_ERR_INVALID_ARG;
   Dims dm;

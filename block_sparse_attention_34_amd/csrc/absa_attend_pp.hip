@@ -130,7 +130,8 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // the bias of its own cluster (-inf where that cluster did not draw the block)
   const float* lwc = PC ? a.wc + (size_t)rowc * a.cap * a.C : nullptr;
   const int ccl = PC ? (lane / SPT) % a.C : 0;
-  const int cq = PC ? (int)a.label[(size_t)rowc * BQ + wq * 32 + qn] : 0;
+  // (no labels: the row is two 64-query blocks, cluster j = block 2i + j of the pair)
+  const int cq = PC ? (a.label ? (int)a.label[(size_t)rowc * BQ + wq * 32 + qn] : (wq >> 1)) : 0;
 
   // ---- direct loads (as in the one-row kernel): buffer resources cover this
   // head's K and V (L*D*2 bytes); rows past L lie past the end of the resource

@@ -43,10 +43,26 @@ struct AttendLaunch {
   int L, d, Bq, Bk, NQ, NK, rows, cap, out_bf16;
   float scale_log2;  // softmax scale times log2(e)
   // per-cluster lists (null wc: one list per row): kv_idx is the union, wc[row][cap][C]
-  // the per-cluster weights, label[row][Bq] each query's cluster
+  // the per-cluster weights, label[row][Bq] each query's cluster (null label with C = 2:
+  // the 128-query row is two 64-query blocks and cluster j holds the queries of block j)
   const float* wc;
   const uint8_t* label;
   int C;
+};
+
+// Pairs of 64-query blocks as 128-query rows: row (bh, i) of NQo = ceil(L/128) takes
+// the lists of 64-query rows bh*NQi + 2i and, if 2i + 1 < NQi, bh*NQi + 2i + 1, and
+// leaves their union (ascending) with one weight per (entry, block), 0 where that
+// block's list lacks the entry.
+struct PairUnionLaunch {
+  const int32_t* count;   // [BH * NQi]
+  const int32_t* kv_idx;  // [BH * NQi][cap]
+  const float* inv_pi;
+  int cap, NK, NQi, NQo, rows_out;
+  int32_t* ucount;        // [rows_out]
+  int32_t* uidx;          // [rows_out][ucap]
+  float* uw;              // [rows_out][ucap][2]
+  int ucap;
 };
 
 struct QuantFp8Launch {
@@ -102,6 +118,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st, hipEvent_t* ev =
 hipError_t configure_select_kernels();
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t st, bool dense);
 hipError_t launch_attend_pp(const AttendLaunch& a, hipStream_t st, bool dense);
+hipError_t launch_pair_union(const PairUnionLaunch& a, hipStream_t st);
 hipError_t launch_quantize_fp8(const QuantFp8Launch& a, hipStream_t st);
 hipError_t launch_attend_fp8(const AttendFp8Launch& a, hipStream_t st, bool dense);
 

@@ -876,21 +876,37 @@ constexpr int SIP_NT = 256;
 // the block.  LDS holds one word per KV block: the cluster mask in the low 8
 // bits, the union position above it.  The weight rows are zeroed with
 // contiguous stores, then each cluster's drawn weights are scattered in.
+// With NQi > 0 the same union is taken over pairs of 64-query rows (C = 2):
+// output row bh NQo + i joins the lists of rows bh NQi + 2i and bh NQi + 2i + 1
+// (the second absent when 2i + 1 = NQi).
 __global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __restrict__ ccount,
                                                                const int32_t* __restrict__ cidx,
                                                                const float* __restrict__ cw, int ccap, int C,
                                                                int NK, int32_t* __restrict__ ucount,
                                                                int32_t* __restrict__ uidx, float* __restrict__ uw,
-                                                               int ucap) {
+                                                               int ucap, int NQo, int NQi) {
   extern __shared__ uint32_t slot[];  // [NK]
   __shared__ int redi[2 * (SIP_NT / 64)];
   const int t = threadIdx.x;
   const size_t row = blockIdx.x;
+  // list j of this row: row C + j, or (NQi > 0: pairs of 64-query blocks) block 2i + j
+  // of head bh for row bh NQo + i, absent past the head's last block
+  auto list_of = [&](int j, int& n) -> size_t {
+    size_t li = row * C + j;
+    bool ok = true;
+    if (NQi > 0) {
+      const size_t bh = row / NQo, i = row % NQo;
+      ok = 2 * i + j < (size_t)NQi;
+      li = bh * NQi + 2 * i + j;
+    }
+    n = ok ? min(ccount[li], ccap) : 0;
+    return li;
+  };
   for (int b = t; b < NK; b += SIP_NT) slot[b] = 0u;
   __syncthreads();
   for (int j = 0; j < C; ++j) {
-    const int n = min(ccount[row * C + j], ccap);
-    const int32_t* li = cidx + (row * C + j) * ccap;
+    int n;
+    const int32_t* li = cidx + list_of(j, n) * ccap;
     for (int e = t; e < n; e += SIP_NT) {
       const int b = li[e];
       if ((unsigned)b < (unsigned)NK) atomicOr(&slot[b], 1u << j);
@@ -917,15 +933,22 @@ __global__ __launch_bounds__(SIP_NT) void cluster_union_kernel(const int32_t* __
   for (int i = t; i < total * C; i += SIP_NT) wrow[i] = 0.f;
   __syncthreads();
   for (int j = 0; j < C; ++j) {
-    const int n = min(ccount[row * C + j], ccap);
-    const int32_t* li = cidx + (row * C + j) * ccap;
-    const float* lw = cw + (row * C + j) * ccap;
+    int n;
+    const size_t lr = list_of(j, n);
+    const int32_t* li = cidx + lr * ccap;
+    const float* lw = cw + lr * ccap;
     for (int e = t; e < n; e += SIP_NT) {
       const int b = li[e];
       if ((unsigned)b < (unsigned)NK) wrow[(size_t)(slot[b] >> 8) * C + j] = lw[e];
     }
   }
   if (t == 0) ucount[row] = total;
+}
+
+hipError_t launch_pair_union(const PairUnionLaunch& a, hipStream_t st) {
+  cluster_union_kernel<<<a.rows_out, SIP_NT, (size_t)a.NK * sizeof(uint32_t), st>>>(
+      a.count, a.kv_idx, a.inv_pi, a.cap, 2, a.NK, a.ucount, a.uidx, a.uw, a.ucap, a.NQo, a.NQi);
+  return hipGetLastError();
 }
 
 // ============================================================================= launchers
@@ -1056,7 +1079,7 @@ hipError_t launch_select(const SelectLaunch& a, hipStream_t st, hipEvent_t* ev) 
   // union of the per-cluster lists
   if (a.per_cluster) {
     cluster_union_kernel<<<rows, SIP_NT, (size_t)a.NK * sizeof(uint32_t), st>>>(
-        a.count, a.kv_idx, a.inv_pi, a.cap, a.C, a.NK, a.ucount, a.uidx, a.uw, a.ucap);
+        a.count, a.kv_idx, a.inv_pi, a.cap, a.C, a.NK, a.ucount, a.uidx, a.uw, a.ucap, 0, 0);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark();
     if (e != hipSuccess) return e;

@@ -207,6 +207,29 @@ absa_status absa_select_profile(const absa_problem* prob, const absa_select_para
 absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, const void* v,
                         const absa_blocklist* lists, void* o, void* stream);
 
+/* Bytes of device workspace absa_attend_pairs needs ([host] pointers): the union
+ * lists of each pair of 64-query blocks, ceil(L/128) per head, NK entries each
+ * (count, indices and two weights per entry).  Same problem rules as
+ * absa_attend_pairs. */
+absa_status absa_attend_pairs_workspace(const absa_problem* prob, size_t* bytes);
+
+/* absa_attend for 64-query blocks (Bq = 64, else ABSA_ERR_UNSUPPORTED; NK <=
+ * 12288), on the 128-query two-row kernel: query blocks 2i and 2i + 1 of a
+ * head form one 128-query row (tokens [128 i, 128 i + 128)) that walks the
+ * ascending union of their two lists, each entry carrying both blocks'
+ * weights, 0 for a block whose list lacks it; each query takes the weight of
+ * its own block, so it attends over exactly its block's list with its
+ * weights, as in absa_attend (the same result up to the order of fp32 sums).
+ * Lists in absa_attend's format (ascending unique indices; entries >= NK
+ * skipped).  workspace: at least absa_attend_pairs_workspace() bytes,
+ * 256-byte aligned, contents on entry ignored, overwritten.  Passages: as
+ * absa_attend; the union with per-member weights is the per-cluster hand-over
+ * below (PIVOT page, section "PIVOT'un arkasındaki iki gözlem"), here with the
+ * two query blocks as the groups. */
+absa_status absa_attend_pairs(const absa_problem* prob, const void* q, const void* k, const void* v,
+                              const absa_blocklist* lists, void* o, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Dense attention softmax(scale Q K^T) V over all L keys, same layouts.
  * Passages: the 3D full attention of the AB-Attention page's section "Video
  * Difüzyon Modellerinde Dikkat (Attention) Darboğazı" (the quantity the
