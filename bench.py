@@ -481,6 +481,25 @@ def main():
         dms = e0.elapsed_time(e1) / 3
         line["dense_ms"] = dms
         line["dense_mfma_frac"] = dense_flops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        if Bq == 128:
+            # the sparse kernel over lists of every block in order, against the dense kernel (the
+            # same tiles): the cost of the list decoding alone; then over the timed SIP lists (the
+            # gathered order as well).  Time per 128-query row and 64-key tile.
+            lists_all = absa.alloc_lists(p)
+            ws_all = torch.empty(absa.select_workspace_bytes(p, 1.0, mode="all"), dtype=torch.uint8, device="cuda")
+            absa.select(p, q, k, 1.0, mode="all", lists=lists_all, workspace=ws_all)
+            absa.attend(p, q, k, v, lists_all, out=o)
+            e0.record(stream)
+            for _ in range(2):
+                absa.attend(p, q, k, v, lists_all, out=o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            all_tiles = float(((lists_all.count.long() * Bk + 63) // 64).double().sum())
+            row_tiles_dense = float(p.rows * (-(-L // 64)))
+            line["row_tile_ns"] = {"dense": dms * 1e6 / row_tiles_dense,
+                                   "sparse_all_blocks": e0.elapsed_time(e1) / 2 * 1e6 / all_tiles,
+                                   "sparse_sip": att_avg * 1e6 / exec_tiles}
+            del lists_all, ws_all
         if Bk == 16 and wl.d == 128 and Bq == 128:
             # the FP8 variant of the attention step on the same lists (not the headline: lower precision)
             for qi8 in (False, True):
