@@ -16,6 +16,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -250,6 +251,22 @@ def measured_traffic(workload_tag="wan14b_720p"):
     return None
 
 
+def measured_clock_ghz():
+    """The sparse attention kernel's clock under load (GHz) from the committed SQ counter summary, if it
+    was taken on the current kernel source (else None)."""
+    prof = os.path.join(ROOT, "profiles", "attend_kernels_wan14b_720p_k4_vs_k5_sq_counters.md")
+    try:
+        text = open(prof).read()
+        if f"`{attend_source_digest()}`" not in text:
+            return None
+        for line in text.splitlines():
+            if line.startswith("| clock under load (GHz) |"):
+                return float(line.split("|")[2])
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
+
+
 def _oracle_sample(wl, keep, kv_block, rows):
     """Seconds the fp64 oracle takes for S1 of one head and for S2-S6 of ``rows``."""
     import numpy as np
@@ -434,7 +451,16 @@ def main():
         "executed_mfma_frac": exec_flops / (att_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "kept_fraction": float(count.double().mean()) / NK,
         "gather_GBs": alg_bytes / (att_avg * 1e-3) / 1e9,
+        "attend_ms_median_min": [statistics.median(att_ms), min(att_ms)],
+        "select_ms_median_min": [statistics.median(sel_ms), min(sel_ms)],
     }
+    # the attention kernel's fraction of the bf16 peak at the clock it runs at under this load
+    # (GRBM_GUI_ACTIVE over the launch in the committed counter summary of the same sources)
+    clk = measured_clock_ghz() if (args.config == 3 and Bk == 16 and not args.heads) else None
+    if clk:
+        peak_clk = MFMA_BF16_PEAK_TFLOPS * clk / 2.4
+        line["roofline_at_measured_clock"] = {"clock_GHz": clk, "peak": peak_clk, "frac": achieved / peak_clk,
+                                              "executed_frac": exec_flops / (att_avg * 1e-3) / 1e12 / peak_clk}
     # the selection kernel by kernel (HIP events between its launches), with the bytes each must
     # move at least: its inputs read once and its outputs written once
     prof = [absa.select_profile(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)[1] for _ in range(3)]
