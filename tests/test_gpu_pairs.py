@@ -3,7 +3,8 @@ over the union of their lists) against the fp64 oracle fed the GPU's own lists: 
 rel-L2 <= 5e-3, on every row of ragged shapes (an odd number of query blocks, so a head's last pair
 holds one block; KV tails inside a tile and, at Bk = 128, in either tile of a block), for SIP, top-k
 and all-block lists; empty lists and entries past NK; bf16 output; sampled rows of the Wan2.1-1.3B
-480p workload; and two runs give the same bytes."""
+480p workload; two runs give the same bytes; and a captured selection + paired attention replays to
+the eager result."""
 import sys
 
 import numpy as np
@@ -113,3 +114,50 @@ def test_pairs_wan13b_480p_sampled_rows(absa):
     lists, _, _ = absa.select(p, dev(wl.q), dev(wl.k), 0.10, seed=0)
     rows = sample_rows(p.nq, wl.H, 40, seed=77)
     _check(absa, wl, p, lists, rows, "pairs Wan2.1-1.3B 480p (sampled rows)")
+
+
+def test_pairs_graph_capture_replays_match_eager(absa):
+    # absa_attend_pairs allocates nothing (its union lists live in the caller's workspace) and
+    # sets no memory, so selection + paired attention can be captured; every replay, with eager
+    # work clobbering the outputs and the workspace in between, reproduces the eager result
+    import torch
+    wl = _workload(2, 5, 15, 16, 128, 16, seed=13)
+    p = problem(wl)
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    lists = absa.alloc_lists(p)
+    ws = torch.empty(absa.select_workspace_bytes(p, 0.2), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(absa.attend_pairs_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    o = torch.empty((p.B, p.H, p.L, p.d), dtype=torch.float32, device="cuda")
+
+    def step():
+        absa.select(p, q, k, 0.2, seed=5, lists=lists, workspace=ws)
+        absa.attend_pairs(p, q, k, v, lists, out=o, workspace=pws)
+
+    def clobber():
+        o.zero_()
+        lists.count.zero_()
+        lists.kv_idx.zero_()
+        lists.inv_pi.zero_()
+        pws.fill_(0xFF)
+
+    clobber()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (lists.count, lists.kv_idx, lists.inv_pi, o)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        clobber()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((lists.count, lists.kv_idx, lists.inv_pi, o), ref):
+            assert torch.equal(a, b), f"replay {i}"

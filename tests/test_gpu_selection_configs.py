@@ -252,3 +252,20 @@ def test_sampler_large_block_counts(absa, grid):
              f"(max rel pi diff {max_rel:.2e}), agreement={agree:.6f} max_abs={err[0]:.3e} rel_l2={err[1]:.3e} "
              f"mean_count={count.mean():.1f}")
         assert agree >= AGREE
+
+
+# ----------------------------------------------------------------------------- measurement entry point
+
+def test_select_profile_gives_the_same_lists(absa):
+    """absa_select_profile: the lists of absa_select, bit for bit, and five positive kernel times."""
+    import torch
+    wl = gen_config(1)
+    p = problem(wl)
+    q, k = dev(wl.q), dev(wl.k)
+    ref, _, _ = absa.select(p, q, k, 0.25, seed=3)
+    got, times = absa.select_profile(p, q, k, 0.25, seed=3)
+    torch.cuda.synchronize()
+    for a, b in zip((got.count, got.kv_idx, got.inv_pi), (ref.count, ref.kv_idx, ref.inv_pi)):
+        assert torch.equal(a, b)
+    assert list(times) == list(absa.SELECT_KERNELS)
+    assert all(t > 0.0 for t in times.values())
