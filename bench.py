@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3, choices=(2, 3, 4),
                     help="2: Wan2.1-1.3B-shaped 480p, 3: Wan2.1-14B-shaped 720p (default), "
                          "4: HunyuanVideo-shaped 720p")
-    ap.add_argument("--keep", type=float, default=None, help="block budget (default: 9.5% for config 3, "
+    ap.add_argument("--keep", type=float, default=None, help="block budget (default: 9.5%% for config 3, "
                                                                   "else the workload's own)")
     ap.add_argument("--kv-block", type=int, default=16)
     ap.add_argument("--heads", type=int, default=0, help="restrict H (0 = all 40)")
