@@ -1,6 +1,7 @@
 """CPU checks of bench.py's host logic: more than one GPU is refused with a message and a non-zero
-status before anything touches a device, and the attention kernel's HBM traffic is reported only while
-the kernel sources are the ones the committed counter summary was taken on."""
+status before anything touches a device, --help prints the options, and the attention kernel's HBM
+traffic is reported only while the kernel sources are the ones the committed counter summary was taken
+on."""
 import os
 import subprocess
 import sys
@@ -13,6 +14,14 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU only" in (r.stdout + r.stderr)
+
+
+def test_help_lists_the_options():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    for opt in ("--gpus", "--steps", "--warmup", "--config", "--keep", "--kv-block", "--extra", "--ablation"):
+        assert opt in r.stdout
 
 
 def test_traffic_is_reported_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
