@@ -251,20 +251,64 @@ def measured_traffic(workload_tag="wan14b_720p"):
     return None
 
 
-def measured_clock_ghz():
-    """The sparse attention kernel's clock under load (GHz) from the committed SQ counter summary, if it
-    was taken on the current kernel source (else None)."""
-    prof = os.path.join(ROOT, "profiles", "attend_kernels_wan14b_720p_k4_vs_k5_sq_counters.md")
+def live_gfx_clock_ghz(launch, n_launch):
+    """Graphics clock (GHz) that AMD SMI reports while ``launch`` runs back to back ``n_launch`` times:
+    the mean over the XCDs' current clocks, averaged over the metric table's refreshes that come after
+    the launches were queued (the table refreshes about once a second, so the launches should cover a
+    few seconds); None if AMD SMI is not available or no refresh fell inside the load.  Runs outside any
+    timed region."""
+    import threading
+    import torch
     try:
-        text = open(prof).read()
-        if f"`{attend_source_digest()}`" not in text:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
             return None
-        for line in text.splitlines():
-            if line.startswith("| clock under load (GHz) |"):
-                return float(line.split("|")[2])
-    except (OSError, ValueError, IndexError):
-        pass
-    return None
+        h = handles[0]
+        readings, done = {}, threading.Event()
+        first = []
+
+        def poll():
+            while not done.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    stamp = m.get("system_clock_counter")
+                    per_xcd = m.get("current_gfxclks")
+                    vals = [x for x in per_xcd if isinstance(x, (int, float)) and 0 < x < 10000] \
+                        if isinstance(per_xcd, (list, tuple)) else []
+                    if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                        vals = [m["current_gfxclk"]]
+                    if vals and isinstance(stamp, (int, float)):
+                        if not first:
+                            first.append(stamp)  # the table as it stood before the load
+                        elif stamp != first[0]:
+                            readings[stamp] = sum(vals) / len(vals)
+                except Exception:
+                    pass
+                done.wait(0.005)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        for _ in range(n_launch):
+            launch()
+        torch.cuda.synchronize()
+        done.set()
+        th.join()
+        if not readings:
+            return None
+        return sum(readings.values()) / len(readings) / 1000.0
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def _oracle_sample(wl, keep, kv_block, rows):
@@ -454,12 +498,16 @@ def main():
         "attend_ms_median_min": [statistics.median(att_ms), min(att_ms)],
         "select_ms_median_min": [statistics.median(sel_ms), min(sel_ms)],
     }
-    # the attention kernel's fraction of the bf16 peak at the clock it runs at under this load
-    # (GRBM_GUI_ACTIVE over the launch in the committed counter summary of the same sources)
-    clk = measured_clock_ghz() if (args.config == 3 and Bk == 16 and not args.heads) else None
+    # the attention kernel's fraction of the bf16 peak at the clock it runs at under this load: the
+    # graphics clock AMD SMI reports while the same launch repeats (after the timed region), else the
+    # GRBM_GUI_ACTIVE clock of the committed counter summary of the same sources
+    clk = live_gfx_clock_ghz(lambda: attend(lists, o), max(4, int(round(3000.0 / max(att_avg, 1e-3)))))
+    clk_src = "AMD SMI current_gfxclk, mean over the XCDs and the metric refreshes during 3 s of repeated " \
+              "attend launches after the timed region"
     if clk:
         peak_clk = MFMA_BF16_PEAK_TFLOPS * clk / 2.4
-        line["roofline_at_measured_clock"] = {"clock_GHz": clk, "peak": peak_clk, "frac": achieved / peak_clk,
+        line["roofline_at_measured_clock"] = {"clock_GHz": clk, "source": clk_src, "peak": peak_clk,
+                                              "frac": achieved / peak_clk,
                                               "executed_frac": exec_flops / (att_avg * 1e-3) / 1e12 / peak_clk}
     # the selection kernel by kernel (HIP events between its launches), with the bytes each must
     # move at least: its inputs read once and its outputs written once
@@ -507,6 +555,9 @@ def main():
         dms = e0.elapsed_time(e1) / 3
         line["dense_ms"] = dms
         line["dense_mfma_frac"] = dense_flops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        dclk = live_gfx_clock_ghz(lambda: absa.dense(p, q, k, v, out=o), max(3, int(round(3000.0 / max(dms, 1e-3)))))
+        if dclk:
+            line["dense_clock_GHz"] = dclk
         if Bq == 128:
             # the sparse kernel over lists of every block in order, against the dense kernel (the
             # same tiles): the cost of the list decoding alone; then over the timed SIP lists (the

@@ -24,6 +24,15 @@ def test_help_lists_the_options():
         assert opt in r.stdout
 
 
+def test_live_clock_is_none_without_a_gpu():
+    # no GPU in this container: the AMD SMI sampler gives up without raising and without launching
+    sys.path.insert(0, ROOT)
+    import bench
+    launched = []
+    assert bench.live_gfx_clock_ghz(lambda: launched.append(1), 3) is None
+    assert not launched
+
+
 def test_traffic_is_reported_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
     sys.path.insert(0, ROOT)
     import bench
@@ -62,21 +71,3 @@ def test_workload_tags_name_the_committed_profiles():
     if os.path.exists(path):
         v = bench.measured_traffic(tag)
         assert v is None or v > 0
-
-
-def test_measured_clock_only_for_the_source_it_was_measured_on(tmp_path, monkeypatch):
-    sys.path.insert(0, ROOT)
-    import bench
-    digest = bench.attend_source_digest()
-    prof = tmp_path / "profiles"
-    prof.mkdir()
-    src = tmp_path / "block_sparse_attention_34_amd" / "csrc"
-    src.mkdir(parents=True)
-    for name in ("absa_attend_tiles.h", "absa_attend.hip", "absa_attend_pp.hip"):
-        (src / name).write_bytes(open(os.path.join(ROOT, "block_sparse_attention_34_amd", "csrc", name), "rb").read())
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    f = prof / "attend_kernels_wan14b_720p_k4_vs_k5_sq_counters.md"
-    f.write_text(f"sources `{digest}`\n| clock under load (GHz) | 1.67 | 1.82 | x |\n")
-    assert bench.measured_clock_ghz() == 1.67
-    f.write_text("sources `0000000000000000`\n| clock under load (GHz) | 1.67 | 1.82 | x |\n")
-    assert bench.measured_clock_ghz() is None
