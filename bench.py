@@ -118,7 +118,7 @@ def ablation(args):
             sel = lambda: absa.select(p, q, k, keep, clusters=clusters, kmeans_steps=steps,  # noqa: E731
                                       seed=seed, mode=mode, lists=lists, workspace=ws)
             t_sel = timed(sel)
-            t_att = timed(lambda: absa.attend(p, q, k, v, lists, out=o))
+            t_att = timed(lambda: absa.attend_balanced(p, q, k, v, lists, out=o))
             err = float(torch.linalg.vector_norm(o - o_dense)) / ref_norm
             kept = float(lists.count.double().mean()) / p.nk
             rows.append((label, Bk, keep, seed, clusters, kept, err, t_sel, t_att))
@@ -398,15 +398,17 @@ def main():
     o = torch.empty((p.B, p.H, p.L, p.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(absa.select_workspace_bytes(p, args.keep), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    # 64-query blocks: adjacent blocks share one 128-query row of the two-row kernel (absa_attend_pairs)
+    # 64-query blocks: adjacent blocks share one 128-query row of the two-row kernel (absa_attend_pairs);
+    # 128-query blocks: the two-row kernel on its persistent grid (absa_attend_balanced)
     pairs = p.q_block == 64
-    pws = torch.empty(absa.attend_pairs_workspace_bytes(p), dtype=torch.uint8, device="cuda") if pairs else None
+    pws = torch.empty(absa.attend_pairs_workspace_bytes(p), dtype=torch.uint8, device="cuda") if pairs else \
+        torch.empty(absa.attend_balanced_workspace_bytes(), dtype=torch.uint8, device="cuda")
 
     def attend(lst, out):
         if pairs:
             absa.attend_pairs(p, q, k, v, lst, out=out, workspace=pws)
         else:
-            absa.attend(p, q, k, v, lst, out=out)
+            absa.attend_balanced(p, q, k, v, lst, out=out, workspace=pws)
 
     def step():
         absa.select(p, q, k, args.keep, seed=0, lists=lists, workspace=ws)
@@ -484,7 +486,7 @@ def main():
         "config": {"workload": wl.name, "B": p.B, "H": p.H, "L": L, "d": d, "grid": [wl.T, wl.Hs, wl.Ws],
                    "q_block": Bq, "kv_block": Bk, "keep": args.keep, "clusters": 4, "kmeans_steps": 3,
                    "selection": "IBCS + SIP", "seed": 0,
-                   "attend": "pairs of 64-query blocks" if pairs else "two-row kernel"},
+                   "attend": "pairs of 64-query blocks" if pairs else "two-row kernel, persistent grid"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(workload_tag(args.config, Bk, args.keep))
@@ -565,10 +567,10 @@ def main():
             lists_all = absa.alloc_lists(p)
             ws_all = torch.empty(absa.select_workspace_bytes(p, 1.0, mode="all"), dtype=torch.uint8, device="cuda")
             absa.select(p, q, k, 1.0, mode="all", lists=lists_all, workspace=ws_all)
-            absa.attend(p, q, k, v, lists_all, out=o)
+            attend(lists_all, o)
             e0.record(stream)
             for _ in range(2):
-                absa.attend(p, q, k, v, lists_all, out=o)
+                attend(lists_all, o)
             e1.record(stream)
             torch.cuda.synchronize()
             all_tiles = float(((lists_all.count.long() * Bk + 63) // 64).double().sum())

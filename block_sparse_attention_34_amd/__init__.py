@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import SEL_ALL, SEL_SIP, SEL_TOPK, AbsaError  # noqa: F401
 
 __all__ = [
-    "Problem", "BlockLists", "select", "select_noalloc", "select_profile", "SELECT_KERNELS", "attend", "attend_pairs",
+    "Problem", "BlockLists", "select", "select_noalloc", "select_profile", "SELECT_KERNELS", "attend",
+    "attend_balanced", "attend_balanced_workspace_bytes", "attend_pairs",
     "attend_pairs_workspace_bytes", "dense", "num_blocks", "select_workspace_bytes",
     "workspace_layout", "alloc_lists", "library", "SEL_SIP", "SEL_TOPK", "SEL_ALL", "AbsaError",
     "Fp8Operands", "alloc_fp8", "fp8_workspace_bytes", "quantize_fp8", "attend_fp8",
@@ -252,6 +253,39 @@ def attend(prob: Problem, q, k, v, lists: BlockLists, out=None):
     st = library().absa_attend(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
                                out.data_ptr(), _stream())
     _lib.check(st, "absa_attend")
+    return out
+
+
+def attend_balanced_workspace_bytes() -> int:
+    """Bytes of workspace ``attend_balanced`` needs (its work queues)."""
+    n = ctypes.c_size_t()
+    _lib.check(library().absa_attend_balanced_workspace(ctypes.byref(n)), "absa_attend_balanced_workspace")
+    return int(n.value)
+
+
+def attend_balanced(prob: Problem, q, k, v, lists: BlockLists, out=None, workspace=None):
+    """``attend`` through absa_attend_balanced: a persistent grid that takes row pairs from per-XCD work
+    queues (the same output as ``attend``).  ``workspace``: a uint8 tensor on Q's GPU of at least
+    attend_balanced_workspace_bytes() bytes (allocated when None).  Returns O [B,H,L,d]."""
+    import torch
+    _check_qkv(prob, q, k, v)
+    _check_lists(prob, lists, q.device, need_cap_nk=False)
+    odt = torch.bfloat16 if prob.out_bf16 else torch.float32
+    if out is None:
+        out = torch.zeros((prob.B, prob.H, prob.L, prob.d), dtype=odt, device=q.device)
+    else:
+        _check_out(prob, out, q.device)
+    nbytes = attend_balanced_workspace_bytes()
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or workspace.device != q.device
+          or workspace.numel() < nbytes):
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes on Q's GPU")
+    p = prob.c()
+    bl = lists.c()
+    st = library().absa_attend_balanced(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(bl),
+                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    _lib.check(st, "absa_attend_balanced")
     return out
 
 

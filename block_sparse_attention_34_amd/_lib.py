@@ -22,6 +22,7 @@ EXPORTED = (
     "absa_fp8_workspace", "absa_quantize_fp8", "absa_attend_fp8",
     "absa_select_clusters_workspace", "absa_select_clusters", "absa_attend_clusters",
     "absa_select_noalloc", "absa_select_profile", "absa_attend_pairs_workspace", "absa_attend_pairs",
+    "absa_attend_balanced_workspace", "absa_attend_balanced",
 )
 
 
@@ -105,6 +106,10 @@ def load() -> ctypes.CDLL:
     lib.absa_attend.argtypes = [P, vp, vp, vp, BL, vp, vp]
     lib.absa_dense.restype = ctypes.c_int
     lib.absa_dense.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.absa_attend_balanced_workspace.restype = ctypes.c_int
+    lib.absa_attend_balanced_workspace.argtypes = [ctypes.POINTER(sz)]
+    lib.absa_attend_balanced.restype = ctypes.c_int
+    lib.absa_attend_balanced.argtypes = [P, vp, vp, vp, BL, vp, vp, sz, vp]
     lib.absa_attend_pairs_workspace.restype = ctypes.c_int
     lib.absa_attend_pairs_workspace.argtypes = [P, ctypes.POINTER(sz)]
     lib.absa_attend_pairs.restype = ctypes.c_int

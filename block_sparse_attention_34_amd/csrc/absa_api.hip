@@ -461,8 +461,20 @@ static bool head_fits_buffer(const absa_problem* p) {
   return (int64_t)p->L * p->d * 2 <= (int64_t)0x7FFFFFF0 - (int64_t)64 * p->d * 2;
 }
 
+// Work queues of the persistent attention grid: 8 counters in a 256-byte region.
+constexpr size_t kQueueBytes = 256;
+
+// Workgroups of the persistent grid: one per compute unit of the current device.
+static int persistent_grid() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 static absa_status attend_common(const absa_problem* prob, const void* q, const void* k, const void* v,
-                                 const absa_blocklist* lists, void* o, void* stream, bool dense) {
+                                 const absa_blocklist* lists, void* o, void* stream, bool dense,
+                                 int32_t* queue = nullptr) {
   Dims dm;
   absa_status st = check_problem(prob, &dm);
   if (st != ABSA_OK) return st;
@@ -494,6 +506,11 @@ static absa_status attend_common(const absa_problem* prob, const void* q, const 
     a.inv_pi = lists->inv_pi;
     a.cap = lists->cap;
   }
+  if (queue && prob->q_block == 128) {
+    a.grid_limit = persistent_grid();
+    if (a.grid_limit <= 0) return ABSA_ERR_HIP;
+    a.queue = queue;
+  }
   hipError_t e = absa::launch_attend(a, static_cast<hipStream_t>(stream), dense);
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }
@@ -506,6 +523,23 @@ absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, 
 absa_status absa_dense(const absa_problem* prob, const void* q, const void* k, const void* v, void* o,
                        void* stream) {
   return attend_common(prob, q, k, v, nullptr, o, stream, true);
+}
+
+absa_status absa_attend_balanced_workspace(size_t* bytes) {
+  if (!bytes) return ABSA_ERR_INVALID_ARG;
+  *bytes = kQueueBytes;
+  return ABSA_OK;
+}
+
+absa_status absa_attend_balanced(const absa_problem* prob, const void* q, const void* k, const void* v,
+                                 const absa_blocklist* lists, void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  Dims dm;
+  absa_status st = check_problem(prob, &dm);
+  if (st != ABSA_OK) return st;
+  if (!workspace || workspace_bytes < kQueueBytes) return ABSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return ABSA_ERR_ALIGNMENT;
+  return attend_common(prob, q, k, v, lists, o, stream, false, static_cast<int32_t*>(workspace));
 }
 
 absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const void* k, const void* v,
@@ -551,7 +585,7 @@ absa_status absa_attend_clusters(const absa_problem* prob, const void* q, const 
 // Pairs of 64-query blocks: the union lists [rows128] count, [rows128][NK] indices
 // and [rows128][NK][2] weights, 256-byte aligned regions.
 struct PairWs {
-  size_t ucount, uidx, uw, total;
+  size_t ucount, uidx, uw, queue, total;
 };
 static PairWs pair_ws(const absa_problem* p, const Dims& dm) {
   const int64_t NQo = (p->L + 127) / 128;
@@ -566,6 +600,7 @@ static PairWs pair_ws(const absa_problem* p, const Dims& dm) {
   w.ucount = take((size_t)rows * 4);
   w.uidx = take((size_t)rows * dm.NK * 4);
   w.uw = take((size_t)rows * dm.NK * 2 * 4);
+  w.queue = take(kQueueBytes);
   w.total = off;
   return w;
 }
@@ -641,6 +676,9 @@ absa_status absa_attend_pairs(const absa_problem* prob, const void* q, const voi
   a.wc = u.uw;
   a.label = nullptr;
   a.C = 2;
+  a.grid_limit = persistent_grid();
+  if (a.grid_limit <= 0) return ABSA_ERR_HIP;
+  a.queue = reinterpret_cast<int32_t*>(ws + w.queue);
   e = absa::launch_attend(a, static_cast<hipStream_t>(stream), false);
   return e == hipSuccess ? ABSA_OK : ABSA_ERR_HIP;
 }

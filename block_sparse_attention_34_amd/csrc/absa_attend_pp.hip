@@ -33,6 +33,36 @@
 
 namespace absa {
 
+// ---- work queues of the persistent grid.  Queue x lists the row pairs the
+// one-workgroup-per-pair grid deals to XCD x (its 32-pair slice of every full
+// run of 256 pairs, then every eighth pair of the partial last run), in that
+// order; a workgroup takes pairs from its own XCD's queue and, once that is
+// empty, from the others in turn, so an XCD that runs slower (they do not all
+// hold the same clock) hands its last pairs to the faster ones.
+__global__ void queue_reset_kernel(int32_t* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
+}
+
+// pair k of queue x, or -1 past its end
+__device__ __forceinline__ int queue_pair(int x, int k, int npairs) {
+  const int nfull = npairs / 256;
+  if (k < 32 * nfull) return (k / 32) * 256 + x * 32 + (k % 32);
+  const int p = nfull * 256 + (k - 32 * nfull) * 8 + x;
+  return p < npairs ? p : -1;
+}
+
+// the next pair for this workgroup, or -1 when every queue is empty
+__device__ __forceinline__ int take_pair(int32_t* queue, int npairs) {
+  constexpr int kXccReg = (3 << 11) | 20;  // s_getreg_b32 operand: HW_REG_XCC_ID, bits [3:0]
+  int x = (int)(__builtin_amdgcn_s_getreg(kXccReg) & 7u);
+  for (int t = 0; t < 8; ++t) {
+    const int p = queue_pair(x, atomicAdd(&queue[x], 1), npairs);
+    if (p >= 0) return p;
+    x = (x + 1) & 7;
+  }
+  return -1;
+}
+
 template <int D, int BK, bool DENSE, bool OUT_BF16, bool PC>
 __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   constexpr int BQ = 128;
@@ -63,9 +93,21 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // Pairs of rows.  Workgroups are dealt round-robin over the 8 XCDs; within a
   // run of 8*32 workgroups, XCD x takes the 32 adjacent pairs [32x, 32x+32), i.e.
   // 64 adjacent query blocks of one head, whose lists overlap in that XCD's L2.
+  // With work queues the grid is persistent: each workgroup takes pairs in the
+  // same XCD order from the queues until they are empty.
   const int npairs = (a.rows + 1) >> 1;
-  int pair = blockIdx.x;
-  {
+  __shared__ int next_pair;
+  for (int pass = 0;; ++pass) {
+  int pair;
+  if (a.queue) {
+    if (threadIdx.x == 0) next_pair = take_pair(a.queue, npairs);
+    __syncthreads();
+    pair = next_pair;
+    __syncthreads();  // (every wave has read it before the next take)
+    if (pair < 0) break;
+  } else {
+    if (pass > 0) break;
+    pair = blockIdx.x;
     constexpr int R = 32, S = 8 * R;
     const int g = pair / S, i = pair % S;
     if ((g + 1) * S <= npairs) pair = g * S + (i & 7) * R + (i >> 3);
@@ -517,11 +559,17 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
         }
     }
   }
+  }  // next pair
 }
 
 template <int D, int BK, bool DENSE>
 static hipError_t launch_pp_t(const AttendLaunch& a, hipStream_t st) {
-  dim3 grid((a.rows + 1) / 2);
+  const int npairs = (a.rows + 1) / 2;
+  dim3 grid(npairs);
+  if (a.queue) {
+    queue_reset_kernel<<<1, 64, 0, st>>>(a.queue);
+    grid = dim3(npairs < a.grid_limit ? npairs : a.grid_limit);
+  }
   if constexpr (!DENSE) {
     if (a.wc) {
       if (a.out_bf16)

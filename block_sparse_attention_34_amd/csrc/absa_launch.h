@@ -48,6 +48,10 @@ struct AttendLaunch {
   const float* wc;
   const uint8_t* label;
   int C;
+  // work queues of the persistent grid (null: one workgroup per row pair): 8 counters,
+  // zeroed on the stream before the attention kernel; grid_limit workgroups (the CU count)
+  int32_t* queue;
+  int grid_limit;
 };
 
 // Pairs of 64-query blocks as 128-query rows: row (bh, i) of NQo = ceil(L/128) takes

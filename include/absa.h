@@ -207,9 +207,30 @@ absa_status absa_select_profile(const absa_problem* prob, const absa_select_para
 absa_status absa_attend(const absa_problem* prob, const void* q, const void* k, const void* v,
                         const absa_blocklist* lists, void* o, void* stream);
 
+/* Bytes of device workspace absa_attend_balanced needs (its work queues),
+ * written to *bytes ([host]); NULL bytes is ABSA_ERR_INVALID_ARG. */
+absa_status absa_attend_balanced_workspace(size_t* bytes);
+
+/* absa_attend on a persistent grid, for 128-query blocks: one workgroup per
+ * compute unit takes row pairs from eight work queues, one per XCD, holding
+ * the pairs absa_attend's one-workgroup-per-pair grid deals to that XCD, in
+ * the same order; once its own queue is empty it takes from the others.  The
+ * output is bit-identical to absa_attend's; the XCDs, which do not all run at
+ * the same clock, then finish together instead of the faster ones idling at
+ * the end.  For 64-query blocks it runs as absa_attend (workspace unused).
+ * workspace: at least absa_attend_balanced_workspace() bytes of device
+ * memory, 256-byte aligned, contents on entry ignored (the call clears its
+ * queues on `stream` before the attention kernel); calls that share a
+ * workspace must not overlap.  Errors as absa_attend, plus ABSA_ERR_WORKSPACE
+ * (NULL or too small) and ABSA_ERR_ALIGNMENT.  Passages: as absa_attend. */
+absa_status absa_attend_balanced(const absa_problem* prob, const void* q, const void* k, const void* v,
+                                 const absa_blocklist* lists, void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Bytes of device workspace absa_attend_pairs needs ([host] pointers): the union
  * lists of each pair of 64-query blocks, ceil(L/128) per head, NK entries each
- * (count, indices and two weights per entry).  Same problem rules as
+ * (count, indices and two weights per entry), and the work queues of its
+ * persistent grid (as absa_attend_balanced).  Same problem rules as
  * absa_attend_pairs. */
 absa_status absa_attend_pairs_workspace(const absa_problem* prob, size_t* bytes);
 

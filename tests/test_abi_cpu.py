@@ -185,9 +185,10 @@ def test_attend_rejects_heads_beyond_32bit_buffer_offsets(lib):
 
 def test_attend_pairs_validation(lib):
     n = ctypes.c_size_t()
-    # 2 heads x ceil(1024 / 128) pairs: counts, [NK] indices and [NK][2] weights, 256-byte regions
+    # 2 heads x ceil(1024 / 128) pairs: counts, [NK] indices and [NK][2] weights, then the work
+    # queues of the persistent grid, 256-byte regions
     assert lib.absa_attend_pairs_workspace(ctypes.byref(prob()), ctypes.byref(n)) == 0
-    assert n.value == 256 + 16 * 64 * 4 + 16 * 64 * 8
+    assert n.value == 256 + 16 * 64 * 4 + 16 * 64 * 8 + 256
     ws = n.value
     assert lib.absa_attend_pairs_workspace(ctypes.byref(prob()), None) == _lib.ABSA_ERR_INVALID_ARG
     assert lib.absa_attend_pairs_workspace(ctypes.byref(prob(q_block=128)), ctypes.byref(n)) == \
@@ -205,6 +206,25 @@ def test_attend_pairs_validation(lib):
     assert a(P, FAKE, FAKE, FAKE, L, FAKE, FAKE, ws - 1, None) == _lib.ABSA_ERR_WORKSPACE
     assert a(P, FAKE, FAKE, FAKE, L, FAKE, FAKE + 16, ws, None) == _lib.ABSA_ERR_ALIGNMENT
     big = prob(L=1 << 23, T=128, Hs=256, Ws=256, d=128)   # L*d*2 = 2^31: beyond 32-bit buffer offsets
+    assert a(ctypes.byref(big), FAKE, FAKE, FAKE, L, FAKE, FAKE, ws, None) == _lib.ABSA_ERR_UNSUPPORTED
+
+
+def test_attend_balanced_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.absa_attend_balanced_workspace(ctypes.byref(n)) == 0
+    assert n.value == 256
+    assert lib.absa_attend_balanced_workspace(None) == _lib.ABSA_ERR_INVALID_ARG
+    ws = n.value
+    a = lib.absa_attend_balanced
+    P, L = ctypes.byref(prob(q_block=128)), ctypes.byref(lists())
+    assert a(P, FAKE, FAKE, FAKE, L, FAKE, None, ws, None) == _lib.ABSA_ERR_WORKSPACE
+    assert a(P, FAKE, FAKE, FAKE, L, FAKE, FAKE, ws - 1, None) == _lib.ABSA_ERR_WORKSPACE
+    assert a(P, FAKE, FAKE, FAKE, L, FAKE, FAKE + 16, ws, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert a(P, FAKE, FAKE, FAKE, L, None, FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert a(P, FAKE, FAKE, FAKE + 4, L, FAKE, FAKE, ws, None) == _lib.ABSA_ERR_ALIGNMENT
+    assert a(P, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None) == _lib.ABSA_ERR_INVALID_ARG
+    assert a(P, FAKE, FAKE, FAKE, ctypes.byref(lists(cap=0)), FAKE, FAKE, ws, None) == _lib.ABSA_ERR_SHAPE
+    big = prob(L=1 << 23, T=128, Hs=256, Ws=256, d=128, q_block=128)   # beyond 32-bit buffer offsets
     assert a(ctypes.byref(big), FAKE, FAKE, FAKE, L, FAKE, FAKE, ws, None) == _lib.ABSA_ERR_UNSUPPORTED
 
 
