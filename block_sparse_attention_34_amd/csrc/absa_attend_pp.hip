@@ -63,7 +63,7 @@ __device__ __forceinline__ int take_pair(int32_t* queue, int npairs) {
   return -1;
 }
 
-template <int D, int BK, bool DENSE, bool OUT_BF16, bool PC>
+template <int D, int BK, bool DENSE, bool OUT_BF16, bool PC, bool PERSIST>
 __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   constexpr int BQ = 128;
   constexpr int HT = 256;              // threads per row
@@ -93,13 +93,15 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // Pairs of rows.  Workgroups are dealt round-robin over the 8 XCDs; within a
   // run of 8*32 workgroups, XCD x takes the 32 adjacent pairs [32x, 32x+32), i.e.
   // 64 adjacent query blocks of one head, whose lists overlap in that XCD's L2.
-  // With work queues the grid is persistent: each workgroup takes pairs in the
-  // same XCD order from the queues until they are empty.
+  // PERSIST: the grid is persistent: each workgroup takes pairs in the same XCD
+  // order from the work queues until they are empty.  (A compile-time switch:
+  // the one-pass instances then hold no loop state, which in this kernel's
+  // scalar registers would spill.)
   const int npairs = (a.rows + 1) >> 1;
   __shared__ int next_pair;
   for (int pass = 0;; ++pass) {
   int pair;
-  if (a.queue) {
+  if constexpr (PERSIST) {
     if (threadIdx.x == 0) next_pair = take_pair(a.queue, npairs);
     __syncthreads();
     pair = next_pair;
@@ -565,24 +567,37 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
 template <int D, int BK, bool DENSE>
 static hipError_t launch_pp_t(const AttendLaunch& a, hipStream_t st) {
   const int npairs = (a.rows + 1) / 2;
-  dim3 grid(npairs);
-  if (a.queue) {
-    queue_reset_kernel<<<1, 64, 0, st>>>(a.queue);
-    grid = dim3(npairs < a.grid_limit ? npairs : a.grid_limit);
-  }
   if constexpr (!DENSE) {
+    if (a.queue) {  // persistent grid over the work queues
+      if (a.grid_limit < 1) return hipErrorInvalidValue;
+      queue_reset_kernel<<<1, 64, 0, st>>>(a.queue);
+      const dim3 grid(npairs < a.grid_limit ? npairs : a.grid_limit);
+      if (a.wc) {
+        if (a.out_bf16)
+          attend_pp_kernel<D, BK, false, true, true, true><<<grid, 512, 0, st>>>(a);
+        else
+          attend_pp_kernel<D, BK, false, false, true, true><<<grid, 512, 0, st>>>(a);
+      } else {
+        if (a.out_bf16)
+          attend_pp_kernel<D, BK, false, true, false, true><<<grid, 512, 0, st>>>(a);
+        else
+          attend_pp_kernel<D, BK, false, false, false, true><<<grid, 512, 0, st>>>(a);
+      }
+      return hipGetLastError();
+    }
     if (a.wc) {
       if (a.out_bf16)
-        attend_pp_kernel<D, BK, false, true, true><<<grid, 512, 0, st>>>(a);
+        attend_pp_kernel<D, BK, false, true, true, false><<<npairs, 512, 0, st>>>(a);
       else
-        attend_pp_kernel<D, BK, false, false, true><<<grid, 512, 0, st>>>(a);
+        attend_pp_kernel<D, BK, false, false, true, false><<<npairs, 512, 0, st>>>(a);
       return hipGetLastError();
     }
   }
+  if (a.queue) return hipErrorInvalidValue;
   if (a.out_bf16)
-    attend_pp_kernel<D, BK, DENSE, true, false><<<grid, 512, 0, st>>>(a);
+    attend_pp_kernel<D, BK, DENSE, true, false, false><<<npairs, 512, 0, st>>>(a);
   else
-    attend_pp_kernel<D, BK, DENSE, false, false><<<grid, 512, 0, st>>>(a);
+    attend_pp_kernel<D, BK, DENSE, false, false, false><<<npairs, 512, 0, st>>>(a);
   return hipGetLastError();
 }
 
