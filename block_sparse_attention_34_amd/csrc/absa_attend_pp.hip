@@ -389,29 +389,6 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
         for (int r = 0; r < 16; ++r) sacc[sb][r] -= shift;
     }
   };
-  // P = 2^t rounded to bf16 in the PV operand layout; returns the row sum of
-  // exactly these rounded values
-  // (packed bf16 pairs: P lives across a barrier, and as a vector of single
-  // bf16 elements it would occupy twice the registers)
-  auto probs = [&]() {
-    float psum = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16x2 pk;
-          pk[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e]);
-          pk[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e + 1]);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, psum, false);
-          w[e] = __builtin_bit_cast(uint32_t, pk);
-        }
-        pf[sb * 2 + hf] = w;
-      }
-    return psum;
-  };
 
   // ---- the two rows' phase sequences on one barrier: row 0 runs vector(0),
   // matrix(0), vector(1), ... while row 1 runs the same sequence one step
@@ -454,19 +431,67 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
     mt = form_logits(t0);
   }
 
-  // vector(m): softmax of tile m -> P(m); then the direct loads of K(m+2) and
-  // V(m+1), after the vector work they would otherwise delay (the four
-  // vector-phase waves of a CU share one address unit, and a wave's in-order
-  // issue stalls behind a queue of loads); then the decoding of tile m+3's
-  // entries and the fetch of tile m+4's
+  // one direct load of a vector phase: chunk j of K(m+2) (j < NCH) or of
+  // V(m+1) (j >= NCH), as dma() issues them
+  auto dma_one = [&](int j, unsigned char* kbuf, unsigned char* vbuf) {
+    const bool isk = j < NCH;
+    const int jj = isk ? j : j - NCH;
+    const int off = (int)((isk ? klane[jj] : vlane[jj]) + (isk ? kn[jj] : vb[jj]));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? krs : vrs, (lds_void_t*)((isk ? kbuf : vbuf) + (jj * NW + wq) * 1024),
+                                             16, off, 0, 0, 0);
+  };
+  // P = 2^t of tile m rounded to bf16 in the PV operand layout (packed bf16
+  // pairs: P lives across a barrier, and as a vector of single bf16 elements it
+  // would occupy twice the registers); returns the row sum of exactly these
+  // rounded values.  SPREAD: the phase's 2 NCH direct loads go out evenly
+  // between the 16 pairs.  The four vector-phase waves of a CU share one
+  // address unit; over gathered blocks, which often miss in L2, it then works
+  // through the loads while the waves form P, where loads issued as a block
+  // after P stall the wave behind their queue at the end of its phase (and
+  // before P, at its start).  The empty statements keep the pairs in this order
+  // between the loads (the row sums stay free to move).  Over contiguous tiles
+  // (dense), which hit in L2, the block after P is faster.
+  auto probs_dma = [&](auto spread, unsigned char* kbuf, unsigned char* vbuf) {
+    constexpr bool SPREAD = decltype(spread)::value;
+    constexpr int EVERY = 16 / (2 * NCH);  // pairs per load
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16x2 pk;
+          pk[0] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e]);
+          pk[1] = (__bf16)__builtin_amdgcn_exp2f(sacc[sb][hf * 8 + 2 * e + 1]);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, psum, false);
+          w[e] = __builtin_bit_cast(uint32_t, pk);
+          if constexpr (SPREAD) {
+            asm volatile("" ::"v"(w[e]));
+            const int c = (sb * 2 + hf) * 4 + e;
+            if (c % EVERY == EVERY - 1) {
+              dma_one(c / EVERY, kbuf, vbuf);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        pf[sb * 2 + hf] = w;
+      }
+    if constexpr (!SPREAD)
+#pragma unroll
+      for (int j = 0; j < 2 * NCH; ++j) dma_one(j, kbuf, vbuf);
+    return psum;
+  };
+  // vector(m): softmax of tile m -> P(m), with the direct loads of K(m+2) and
+  // V(m+1) spread between its pairs; then the decoding of tile m+3's entries
+  // and the fetch of tile m+4's
   // (pc: the parity of m as a compile-time constant, which names the slots)
   auto vector_phase = [&](auto pc, int m) {
     constexpr int p = decltype(pc)::value;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     rescale(mt, m_use);
-    l_run += probs();
-    dma(krs, klane, kn, p ? K1 : K0);  // K(m+2)
-    dma(vrs, vlane, vb, p ? V0 : V1);  // V(m+1)
+    l_run += probs_dma(std::integral_constant<bool, !DENSE>(), p ? K1 : K0, p ? V0 : V1);  // K(m+2), V(m+1)
 #pragma unroll
     for (int q = 0; q < NCH; ++q) vb[q] = kn[q];
     decode(EN, m + 3, kn, t3);
