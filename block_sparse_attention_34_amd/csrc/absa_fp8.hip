@@ -682,18 +682,6 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
         for (int r = 0; r < 16; ++r) sacc[sb][r] -= sh8;
     }
   };
-  // ExpCast: byte = sat_u8(rne(y)), four per dword
-  auto probs = [&]() {
-#pragma unroll
-    for (int dw = 0; dw < 8; ++dw) {
-      const int sb = dw >> 2, r0 = 4 * (dw & 3);
-      uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0], 0, 0u);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 1], 1, w);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 2], 2, w);
-      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 3], 3, w);
-      pf[dw] = (int)w;
-    }
-  };
 
   // ---- pipeline state (as in the bf16 two-row kernel): entering vector(m),
   // sacc holds y of tile m and mt its lane max; t1, t2 are tiles m+1, m+2;
@@ -726,6 +714,51 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
     qk(K0);
     mt = form_logits(t0, K0);
   }
+  // one direct load of a vector phase, in dma()'s order: the K chunks, s_K, the
+  // V chunks, the block means
+  auto dma_one = [&](int i, unsigned char* kbuf, unsigned char* vbuf) {
+    if (i < NCH) {
+      const int off = (int)(klane[i] + kn.kv[i]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(kbuf + (i * NW + wq) * 1024), 16, off, 0, 0, 0);
+    } else if (i == NCH) {
+      const int off = (int)kn.sk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void_t*)(kbuf + KT + wq * 256), 4, off, 0, 0, 0);
+    } else if (i < 2 * NCH + 1) {
+      const int j = i - NCH - 1;
+      const int off = (int)(vlane[j] + vb.kv[j]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(vbuf + (j * NW + wq) * 1024), 16, off, 0, 0, 0);
+    } else {
+      const int off = (int)(mlane + vb.mu);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (lds_void_t*)(vbuf + VT + wq * 256), 4, off, 0, 0, 0);
+    }
+  };
+  // ExpCast: byte = sat_u8(rne(y)), four per dword.  Over gathered lists the
+  // phase's 2 NCH + 2 direct loads go out one after each of the first dwords, so
+  // that the CU's shared address unit works through them while the waves convert
+  // (as one block the compiler issues them ahead of the conversions, and each
+  // wave then stalls behind the queue); the empty statements keep the dwords in
+  // this order.  Dense tiles hit in L2 and keep the block.
+  auto probs_dma = [&](unsigned char* kbuf, unsigned char* vbuf) {
+#pragma unroll
+    for (int dw = 0; dw < 8; ++dw) {
+      const int sb = dw >> 2, r0 = 4 * (dw & 3);
+      uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0], 0, 0u);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 1], 1, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 2], 2, w);
+      w = __builtin_amdgcn_cvt_pk_u8_f32(sacc[sb][r0 + 3], 3, w);
+      pf[dw] = (int)w;
+      if constexpr (!DENSE) {
+        asm volatile("" ::"v"(w));
+        if (dw < 2 * NCH + 2) {
+          dma_one(dw, kbuf, vbuf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if constexpr (DENSE)
+#pragma unroll
+      for (int i = 0; i < 2 * NCH + 2; ++i) dma_one(i, kbuf, vbuf);
+  };
   // loads issued by one vector phase: K (NCH) and V (NCH) direct loads, the
   // s_K and block-mean loads, and (lists) two entry loads
   constexpr int NLD = 2 * NCH + 2 + (DENSE ? 0 : 2);
@@ -734,9 +767,7 @@ __global__ __launch_bounds__(512, 1) void attend_fp8_kernel(AttendFp8Launch a) {
     constexpr int p = decltype(pc)::value;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     rescale(mt, m_use);
-    probs();
-    dma(kn, p ? K1 : K0, nullptr, true, false);  // K(m+2)
-    dma(vb, nullptr, p ? V0 : V1, false, true);  // V(m+1) and its block means
+    probs_dma(p ? K1 : K0, p ? V0 : V1);  // K(m+2), V(m+1) and its block means
     vb = kn;
     decode(EN, m + 3, kn, t3);
     fetch(EN, m + 4);
