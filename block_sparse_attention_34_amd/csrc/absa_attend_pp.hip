@@ -470,8 +470,9 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
           if constexpr (SPREAD) {
             asm volatile("" ::"v"(w[e]));
             const int c = (sb * 2 + hf) * 4 + e;
-            if (c % EVERY == EVERY - 1) {
-              dma_one(c / EVERY, kbuf, vbuf);
+            // load i after pair EVERY (i + 1), the last one after the final pair
+            if ((c > 0 && c % EVERY == 0) || c == 15) {
+              dma_one(c == 15 ? 2 * NCH - 1 : c / EVERY - 1, kbuf, vbuf);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
