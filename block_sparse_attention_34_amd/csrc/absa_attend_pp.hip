@@ -446,11 +446,12 @@ __global__ __launch_bounds__(512, 1) void attend_pp_kernel(AttendLaunch a) {
   // rounded values.  SPREAD: the phase's 2 NCH direct loads go out evenly
   // between the 16 pairs.  The four vector-phase waves of a CU share one
   // address unit; over gathered blocks, which often miss in L2, it then works
-  // through the loads while the waves form P, where loads issued as a block
-  // after P stall the wave behind their queue at the end of its phase (and
-  // before P, at its start).  The empty statements keep the pairs in this order
+  // through the loads while the waves form P, where with the loads as one block
+  // (which the compiler schedules ahead of the exponentials) each wave stalls
+  // behind their queue.  The empty statements keep the pairs in this order
   // between the loads (the row sums stay free to move).  Over contiguous tiles
-  // (dense), which hit in L2, the block after P is faster.
+  // (dense), which hit in L2, the compiler's own placement of the block is
+  // faster.
   auto probs_dma = [&](auto spread, unsigned char* kbuf, unsigned char* vbuf) {
     constexpr bool SPREAD = decltype(spread)::value;
     constexpr int EVERY = 16 / (2 * NCH);  // pairs per load
